@@ -1,0 +1,202 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so, the PagedAttention hot path for AMD
+ * Instinct MI355X (gfx950, CDNA4).
+ *
+ * The problem these calls solve is stated on the pages this library follows:
+ *   - gaoleia.github.io "PagedAttention 和 Continuous Batching": §1.3 (a
+ *     physical block holds block_size tokens of K and of V, each token a
+ *     [num_heads, head_dim] row), §1.4 (a per-request block table maps
+ *     logical block i to a physical block), §1.5 (slot mapping), §1.6 (paged
+ *     attention: gather each sequence's blocks in logical order, keep seq_len
+ *     tokens, softmax(q K^T / sqrt(d)) V), §2.4-§2.5 (one step mixes decode
+ *     rows with 512-token prefill chunks);
+ *   - feifeigd.github.io "vLLM 架构详解", 一 PagedAttention (append_token writes
+ *     a new token's K/V at its in-block position).
+ *
+ * Conventions shared by every call
+ *   Memory.   Every pointer argument is a DEVICE pointer owned by the caller;
+ *             the library allocates and frees nothing and keeps no state
+ *             other than a thread-local error string and process-wide tuning
+ *             knobs.  Buffers must stay alive until the enqueued work ends.
+ *   Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ *             stream).  Calls only enqueue kernels (at most two per call) and
+ *             never synchronise.
+ *   Errors.   Arguments are validated on the host before anything is
+ *             enqueued: a call that returns non-zero has enqueued nothing,
+ *             except PKV_EHIP (the launch itself failed).  pkv_last_error()
+ *             then describes the failure.
+ *   Device contents that cannot be checked without a sync (block ids,
+ *             seq_lens, positions, slots) are clamped so that no access leaves
+ *             the caller's buffers; values outside their documented range give
+ *             unspecified (but memory-safe) results.
+ *   Layouts.  All arrays are dense and row-major.  KV pools are
+ *             [num_blocks, block_size, num_kv_heads, head_dim]: the K (or V)
+ *             row of token `off` of physical block `b` for KV head `h` starts
+ *             at element ((b*block_size + off)*num_kv_heads + h)*head_dim.
+ *             block_tables is int32 [num_seqs, max_blocks_per_seq]; entries past
+ *             a sequence's last block are ignored (pad them with -1).
+ *   Types.    dtype PKV_BF16 means query/key/value/caches hold bfloat16,
+ *             PKV_F32 float32; outputs are always float32; accumulation is
+ *             float32.  Pointers to data must be 16-byte aligned.
+ *   GQA.      Query head hq reads KV head hq / (num_q_heads / num_kv_heads).
+ *   Support.  head_dim in {64, 128}; block_size in {16, 32};
+ *             num_q_heads % num_kv_heads == 0.  Other values return
+ *             PKV_EUNSUPPORTED.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,        /* bad pointer, size or alignment                  */
+  PKV_EUNSUPPORTED = 2,  /* valid but not built (head_dim, block_size, ...)  */
+  PKV_EWORKSPACE = 3,    /* workspace missing or smaller than required      */
+  PKV_EHIP = 4           /* a HIP runtime call failed                       */
+} pkv_status;
+
+/* Library version, major*10000 + minor*100 + patch. */
+int pkv_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* pkv_status_string(int status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* pkv_last_error(void);
+
+/*
+ * Slot mapping (gaoleia "PagedAttention 和 Continuous Batching" §1.5).
+ *   For every new token t, let s be the sequence with
+ *   query_start_loc[s] <= t < query_start_loc[s+1] and p = positions[t]:
+ *     slot_mapping[t] = block_tables[s][p / block_size] * block_size
+ *                       + p % block_size
+ *   p < 0 (padding) gives -1, and so does a token outside every sequence or
+ *   a position whose logical block is past max_blocks_per_seq or holds a
+ *   negative id.
+ *   block_tables    int32 [num_seqs, max_blocks_per_seq]      (device, read)
+ *   positions       int32 [num_tokens]                        (device, read)
+ *   query_start_loc int32 [num_seqs + 1], non-decreasing, 0 first (device)
+ *   slot_mapping    int64 [num_tokens]                        (device, written)
+ *   num_tokens may be 0 (nothing is enqueued).
+ */
+int pkv_compute_slot_mapping(const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                             const int32_t* positions, const int32_t* query_start_loc,
+                             int32_t num_tokens, int32_t block_size, int64_t* slot_mapping,
+                             void* stream);
+
+/*
+ * reshape_and_cache: write each new token's K and V rows into its slot
+ * (feifeigd "vLLM 架构详解" 一 PagedAttention, append_token / _write_kv;
+ * gaoleia §2.4, the decode step appends K6,V6 before attending).
+ *   key, value              [num_tokens, num_kv_heads, head_dim]  (device, read)
+ *   key_cache, value_cache  [num_blocks, block_size, num_kv_heads, head_dim]
+ *                           (device, rows at the slots overwritten in place)
+ *   slot_mapping            int64 [num_tokens]; -1 = skip this token; slots
+ *                           >= num_blocks*block_size are skipped too.
+ *   A bit copy (no conversion): key/value and the caches share `dtype`.
+ *   Duplicate slots are a caller error (the winner is unspecified).
+ */
+int pkv_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                          const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int64_t num_blocks, int32_t block_size, pkv_dtype dtype,
+                          void* stream);
+
+/*
+ * Bytes of device workspace pkv_paged_attention_decode needs for this shape
+ * on the CURRENT device (the split of the work depends on its compute-unit
+ * count).  Returns 0 for shapes the library does not support.
+ */
+size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, pkv_dtype dtype);
+
+/*
+ * Paged decode attention (gaoleia §1.6): one query row per sequence.
+ *   out[s][hq][:] = sum_j softmax_j(scale * q[s][hq] . K_j) V_j over the
+ *   first seq_lens[s] tokens j of sequence s, K_j/V_j being the rows of KV head
+ *   hq / (num_q_heads / num_kv_heads) found through block_tables[s].
+ *   out          float32 [num_seqs, num_q_heads, head_dim]   (device, written)
+ *   query        [num_seqs, num_q_heads, head_dim] of dtype  (device, read)
+ *   key_cache, value_cache  pools as above (device, read)
+ *   block_tables int32 [num_seqs, max_blocks_per_seq]; seq_lens int32 [num_seqs]
+ *   seq_lens[s] == 0 gives a zero row.  seq_lens are clamped to
+ *   max_blocks_per_seq*block_size; block ids to [0, num_blocks).
+ *   max_seq_len  an upper bound of seq_lens (host scalar, used for sizing;
+ *                0 is allowed and then every row is zero).
+ *   workspace    >= pkv_decode_workspace_size(...) bytes, 256-byte aligned,
+ *                contents ignored on entry.  Long sequences are split over
+ *                several workers (split-K); a second kernel merges the parts.
+ *   num_seqs <= 8192.
+ */
+int pkv_paged_attention_decode(float* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
+                               pkv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace pkv_paged_attention_varlen needs (current device).
+ */
+size_t pkv_varlen_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
+                                 int32_t block_size, pkv_dtype dtype);
+
+/*
+ * Varlen attention for a step that mixes prefill chunks and decode rows
+ * (gaoleia §2.4-§2.5; fanquanpp.github.io "vLLM服务内部" 分块预填充).
+ *   Sequence s owns query rows query_start_loc[s] .. query_start_loc[s+1]-1
+ *   (q_s rows).  Row i of it sits at position seq_lens[s] - q_s + i and
+ *   attends keys 0 .. that position (causal mask aligned to the end of the
+ *   key range, so a chunk after c cached tokens sees c + i + 1 keys).  The K/V
+ *   of the step's own tokens must already be in the cache
+ *   (pkv_reshape_and_cache first).
+ *   out    float32 [num_tokens, num_q_heads, head_dim]  (device, written)
+ *   query  [num_tokens, num_q_heads, head_dim] of dtype (device, read)
+ *   query_start_loc int32 [num_seqs + 1] with query_start_loc[num_seqs] ==
+ *   num_tokens; max_query_len >= every q_s (host scalar); seq_lens[s] >= q_s.
+ *   Rows of a sequence with seq_lens[s] < q_s are unspecified.
+ *   workspace >= pkv_varlen_workspace_size(...) bytes, 256-byte aligned.
+ *   num_seqs <= 8192.
+ */
+int pkv_paged_attention_varlen(float* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                               const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                               int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                               int32_t block_size, float scale, pkv_dtype dtype, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement and test knobs (process-wide; not needed for normal use).
+ *
+ * pkv_set_profile_events: when both are non-NULL, every later attention call
+ * on this thread records `start` (a hipEvent_t) right before its main
+ * attention kernel and `stop` right after it, on the call's stream, so a
+ * caller can time that kernel alone.  NULL, NULL turns it off.
+ *
+ * pkv_set_decode_workers: number of workers (wavefronts) the decode split
+ * uses; 0 restores the default (compute units x pkv_get_waves_per_cu()).
+ * The workspace size follows the setting.  Used by tests to force many
+ * different split points.  Returns the previous value.
+ *
+ * pkv_set_waves_per_cu: default worker density per compute unit (4..16,
+ * multiple of 4; default 8).  Returns the previous value.
+ */
+int pkv_set_profile_events(void* start_event, void* stop_event);
+int pkv_set_decode_workers(int32_t workers);
+int pkv_set_waves_per_cu(int32_t waves);
+int pkv_get_waves_per_cu(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDKV_H */

@@ -1,0 +1,252 @@
+// C ABI of libpagedkv.so: argument validation, sizing and kernel dispatch.
+// Every check runs on the host before anything is enqueued.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+#include <cmath>
+
+#include "../../include/pagedkv.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
+std::atomic<int> g_workers_override{0};
+std::atomic<int> g_waves_per_cu{8};
+
+constexpr int kMaxSeqs = 8192;
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return PKV_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(pkv_dtype dt) { return dt == PKV_BF16 ? 2 : 4; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Compute units of the current device (0 on failure).
+int current_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return cus;
+}
+
+int decode_workers() {
+  const int forced = g_workers_override.load();
+  if (forced > 0) return forced;
+  int cus = current_cus();
+  if (cus <= 0) cus = 256;
+  return cus * g_waves_per_cu.load();
+}
+
+int check_shape(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                pkv_dtype dtype) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0)
+    return fail(PKV_EINVAL, "head counts must be positive (%d, %d)", num_q_heads, num_kv_heads);
+  if (num_q_heads % num_kv_heads)
+    return fail(PKV_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, num_kv_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+  if (block_size != 16 && block_size != 32)
+    return fail(PKV_EUNSUPPORTED, "block_size %d (supported: 16, 32)", block_size);
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "dtype %d", (int)dtype);
+  return PKV_OK;
+}
+
+// Upper bound of the chunk count the split sees, times the worker count, must
+// stay far inside int64 (the kernels multiply the two).
+bool split_fits(int64_t num_seqs, int64_t pairs_per_seq, int64_t max_tokens, int64_t workers) {
+  const int64_t chunks = num_seqs * pairs_per_seq * ((max_tokens + 31) / 32);
+  return chunks < (int64_t(1) << 40) && workers <= 65536;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_version(void) { return 100; }
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_EINVAL: return "PKV_EINVAL: invalid argument";
+    case PKV_EUNSUPPORTED: return "PKV_EUNSUPPORTED: unsupported configuration";
+    case PKV_EWORKSPACE: return "PKV_EWORKSPACE: workspace missing or too small";
+    case PKV_EHIP: return "PKV_EHIP: HIP runtime error";
+    default: return "unknown pkv status";
+  }
+}
+
+const char* pkv_last_error(void) { return g_err; }
+
+int pkv_set_profile_events(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(PKV_EINVAL, "profile events must be both set or both NULL");
+  g_ev_start = static_cast<hipEvent_t>(start_event);
+  g_ev_stop = static_cast<hipEvent_t>(stop_event);
+  return ok();
+}
+
+int pkv_set_decode_workers(int32_t workers) {
+  if (workers < 0 || workers > 65536) return -1;
+  return g_workers_override.exchange(workers);
+}
+
+int pkv_set_waves_per_cu(int32_t waves) {
+  if (waves < 4 || waves > 16 || waves % 4) return -1;
+  return g_waves_per_cu.exchange(waves);
+}
+
+int pkv_get_waves_per_cu(void) { return g_waves_per_cu.load(); }
+
+int pkv_compute_slot_mapping(const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                             const int32_t* positions, const int32_t* query_start_loc,
+                             int32_t num_tokens, int32_t block_size, int64_t* slot_mapping,
+                             void* stream) {
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq < 0)
+    return fail(PKV_EINVAL, "negative size (num_tokens %d, num_seqs %d, max_blocks %d)", num_tokens,
+                num_seqs, max_blocks_per_seq);
+  if (block_size <= 0) return fail(PKV_EINVAL, "block_size %d", block_size);
+  if (num_tokens == 0) return ok();
+  if (!positions || !query_start_loc || !slot_mapping || (num_seqs > 0 && max_blocks_per_seq > 0 && !block_tables))
+    return fail(PKV_EINVAL, "null pointer");
+  hipError_t e = pkv::launch_slot_mapping(block_tables, num_seqs, max_blocks_per_seq, positions,
+                                          query_start_loc, num_tokens, block_size, slot_mapping,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "slot_mapping launch");
+}
+
+int pkv_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                          const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int64_t num_blocks, int32_t block_size, pkv_dtype dtype,
+                          void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks < 0 || block_size <= 0)
+    return fail(PKV_EINVAL, "bad size (tokens %d, kv_heads %d, head_dim %d, blocks %lld, block_size %d)",
+                num_tokens, num_kv_heads, head_dim, (long long)num_blocks, block_size);
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "dtype %d", (int)dtype);
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * elem_bytes(dtype);
+  if (row_bytes % 16) return fail(PKV_EUNSUPPORTED, "token row of %lld bytes is not a multiple of 16", (long long)row_bytes);
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return fail(PKV_EINVAL, "null pointer");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PKV_EINVAL, "key/value/cache pointers must be 16-byte aligned");
+  hipError_t e = pkv::launch_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                                               (int)row_bytes, num_blocks * block_size,
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "reshape_and_cache launch");
+}
+
+size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, pkv_dtype dtype) {
+  if (num_seqs < 0 || num_seqs > kMaxSeqs) return 0;
+  if (check_shape(num_q_heads, num_kv_heads, head_dim, block_size, dtype) != PKV_OK) return 0;
+  return pkv::decode_workspace_bytes(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim,
+                                     decode_workers());
+}
+
+static int run_decode(float* out, const void* query, const void* key_cache, const void* value_cache,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                      const int32_t* qsl, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t max_seq_len,
+                      float scale, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  const int group = num_q_heads / num_kv_heads;
+  const int workers = decode_workers();
+  const int head_tiles = (group + 15) / 16;
+  if (!split_fits(num_seqs, (int64_t)num_kv_heads * head_tiles,
+                  (int64_t)max_blocks_per_seq * block_size, workers))
+    return fail(PKV_EUNSUPPORTED, "problem too large for the split arithmetic");
+  const size_t need = pkv::decode_workspace_bytes(num_seqs, num_kv_heads, group, head_dim, workers);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.qsl = qsl;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.head_tiles = head_tiles;
+  a.tile_cols = group < 16 ? group : 16;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.workers = workers;
+  pkv::decode_workspace_carve(a, workspace, head_dim);
+  (void)max_seq_len;
+  hipError_t e = pkv::launch_decode(a, head_dim, block_size, dtype == PKV_BF16, stream, g_ev_start, g_ev_stop);
+  return e == hipSuccess ? ok() : hip_fail(e, "decode launch");
+}
+
+int pkv_paged_attention_decode(float* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
+                               pkv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_seqs > kMaxSeqs) return fail(PKV_EUNSUPPORTED, "num_seqs %d (max %d)", num_seqs, kMaxSeqs);
+  if (max_blocks_per_seq < 0 || num_blocks < 0 || max_seq_len < 0)
+    return fail(PKV_EINVAL, "negative size");
+  if (num_seqs == 0) return ok();
+  if (!out || !query || !seq_lens || (max_blocks_per_seq > 0 && (!block_tables || !key_cache || !value_cache)))
+    return fail(PKV_EINVAL, "null pointer");
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PKV_EINVAL, "out/query/cache pointers must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale is not finite");
+  if (max_blocks_per_seq > 0 && num_blocks == 0) return fail(PKV_EINVAL, "empty pool with a non-empty block table");
+  return run_decode(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens, nullptr,
+                    num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_seq_len,
+                    scale, dtype, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t pkv_varlen_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
+                                 int32_t block_size, pkv_dtype dtype) {
+  (void)num_tokens;
+  (void)max_query_len;
+  return pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dtype);
+}
+
+int pkv_paged_attention_varlen(float* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                               const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                               int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                               int32_t block_size, float scale, pkv_dtype dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  (void)out; (void)query; (void)key_cache; (void)value_cache; (void)block_tables; (void)max_blocks_per_seq;
+  (void)seq_lens; (void)query_start_loc; (void)num_seqs; (void)num_tokens; (void)max_query_len;
+  (void)max_seq_len; (void)num_q_heads; (void)num_kv_heads; (void)head_dim; (void)num_blocks;
+  (void)block_size; (void)scale; (void)dtype; (void)workspace; (void)workspace_bytes; (void)stream;
+  return fail(PKV_EUNSUPPORTED, "varlen attention is not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Slot mapping and the cache write (reshape_and_cache).
+//
+// Slot arithmetic: gaoleia.github.io "PagedAttention 和 Continuous Batching"
+// §1.5 (logical block = pos / block_size, offset = pos % block_size,
+// slot = table[logical block] * block_size + offset).  Cache write: feifeigd
+// "vLLM 架构详解" 一 PagedAttention (a new token's K/V goes to its in-block
+// position of its block) and gaoleia §1.3 (block layout [block_size, heads,
+// head_dim]), so a slot's K row for all KV heads is one contiguous
+// num_kv_heads*head_dim run of the pool.
+//
+// Both kernels are pure data movement bounded by launch latency at serving
+// sizes; the write moves 16 bytes per lane with fully coalesced rows.
+#include "common.h"
+#include "launch.h"
+
+namespace pkv {
+
+__global__ void __launch_bounds__(256)
+slot_mapping_kernel(const int32_t* __restrict__ block_tables, int num_seqs, int max_blocks,
+                    const int32_t* __restrict__ positions, const int32_t* __restrict__ qsl,
+                    int num_tokens, int block_size, int64_t* __restrict__ slots) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= num_tokens) return;
+  // sequence owning row t: the last s with qsl[s] <= t
+  int lo = 0, hi = num_seqs;  // invariant: qsl[lo] <= t (qsl[0] == 0), answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (qsl[mid] <= t) lo = mid; else hi = mid;
+  }
+  int64_t slot = -1;
+  const int p = positions[t];
+  if (num_seqs > 0 && t < qsl[lo + 1] && p >= 0) {
+    const int lb = p / block_size;
+    if (lb < max_blocks) {
+      const int phys = block_tables[(int64_t)lo * max_blocks + lb];
+      if (phys >= 0) slot = (int64_t)phys * block_size + (p - lb * block_size);
+    }
+  }
+  slots[t] = slot;
+}
+
+// One lane moves 16 bytes of K and 16 bytes of V; a token row is
+// row_vecs*16 bytes (num_kv_heads*head_dim*elem).
+__global__ void __launch_bounds__(256)
+reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
+                         u32x4* __restrict__ key_cache, u32x4* __restrict__ value_cache,
+                         const int64_t* __restrict__ slots, int64_t total, int row_vecs,
+                         int64_t num_slots) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / row_vecs;
+    const int64_t c = i - t * row_vecs;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    const u32x4 k = key[i];
+    const u32x4 v = value[i];
+    key_cache[slot * row_vecs + c] = k;
+    value_cache[slot * row_vecs + c] = v;
+  }
+}
+
+hipError_t launch_slot_mapping(const int32_t* bt, int num_seqs, int max_blocks, const int32_t* pos,
+                               const int32_t* qsl, int num_tokens, int block_size, int64_t* slots,
+                               hipStream_t stream) {
+  const int threads = 256;
+  const int blocks = (num_tokens + threads - 1) / threads;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(blocks), dim3(threads), 0, stream, bt, num_seqs,
+                     max_blocks, pos, qsl, num_tokens, block_size, slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
+                                    const int64_t* slots, int num_tokens, int row_bytes,
+                                    int64_t num_slots, hipStream_t stream) {
+  const int row_vecs = row_bytes / 16;
+  const int64_t total = (int64_t)num_tokens * row_vecs;
+  const int threads = 256;
+  int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                     (const u32x4*)key, (const u32x4*)value, (u32x4*)kc, (u32x4*)vc, slots, total,
+                     row_vecs, num_slots);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,533 @@
+// Paged decode attention for gfx950: a split kernel that walks block tables
+// and a reduction kernel that merges split parts.
+//
+// What is computed (gaoleia.github.io "PagedAttention 和 Continuous
+// Batching" §1.6): for sequence s and query head hq, gather the first
+// seq_len tokens' K and V rows of KV head hq / G through the block table in
+// logical order and return softmax(scale * q K^T) V.  Paging changes where K/V
+// live, not the result.  Decode time is spent reading the KV cache (same
+// page, §2.4), so the kernel is built around HBM streaming.
+//
+// Design (MI355X-first; the pages give no kernel):
+//  * Work unit = one 32-token chunk of one (sequence, KV head, head tile)
+//    "pair".  All chunks of all pairs are laid end to end and cut into
+//    `workers` equal contiguous ranges, one per wavefront (stream-K style),
+//    so every wave streams the same number of KV bytes whatever the length
+//    mix.  A wave whose range covers a whole pair writes the final row; other
+//    ranges leave an unnormalised part (max, sum, output) in the workspace
+//    and the reduction kernel merges the parts of each pair.
+//  * Each wave serves all G query heads that share its KV head, so every K/V
+//    byte is read once per step (GQA grouping).  Up to 16 heads form the N
+//    side of the MFMA tiles:
+//      S^T[token, head] = K[token, :] . Q[head, :]         (A = K rows)
+//      O^T[dim, head]  += V^T[dim, token] P^T[token, head]  (A = V rows)
+//    With tokens on M, the S^T accumulator already has each lane's P values
+//    in the k-slots of the P^T operand, and each head's softmax state lives
+//    in the lanes that own its O^T column; no LDS round trip is needed.
+//  * K rows are loaded straight into MFMA A-operand registers (16 B per lane,
+//    64 B runs per row).  V is loaded as whole 256-byte head rows (16 lanes x
+//    16 B, four rows per instruction) and transposed inside each lane with
+//    v_perm_b32 into the A operand of the PV product.
+//  * bf16 uses v_mfma_f32_16x16x32_bf16 with P rounded to bf16; fp32 uses
+//    v_mfma_f32_16x16x4_f32 and keeps P in fp32.
+//  * Online softmax in the log2 domain: per chunk the max over tokens is
+//    reduced across the four 16-lane rows with two cross-lane xors; the sum
+//    stays lane-local until the end.  Masked tokens are excluded by select
+//    and their V rows zeroed, so stale NaN slots never reach a product.
+//  * Block ids: each wave holds a 64-entry window of its block-table row in
+//    one VGPR and reads entries with v_readlane; loads of chunk n+1 are in
+//    flight while chunk n is computed (bf16).
+#include "common.h"
+#include "launch.h"
+
+namespace pkv {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int N> struct U32Vec;
+template <> struct U32Vec<2> { typedef u32x2 type; };
+template <> struct U32Vec<4> { typedef u32x4 type; };
+
+// ------------------------------------------------------------------ bf16 tile
+template <int D_, int BS_>
+struct TileBf16 {
+  static constexpr int D = D_;
+  static constexpr int BS = BS_;
+  static constexpr bool kDoubleBuffer = true;
+  static constexpr int KK = D / 32;   // K=32 slices of the QK contraction
+  static constexpr int VW = D / 16;   // dims per lane of a V row (= O^T dim tiles)
+  static constexpr int NDT = D / 16;
+  typedef uint16_t Elem;
+  typedef typename U32Vec<VW / 2>::type VVec;
+
+  struct Q { u32x4 q[KK]; };
+  struct Buf { u32x4 k[2][KK]; VVec v[2][4]; };
+
+  // Query head `i` (lane % 16) of the tile, slice kk: dims 32kk + 8c .. +7.
+  static __device__ __forceinline__ void load_q(Q& q, const Elem* qb, int cols) {
+    const int l = lane_id(), i = l & 15, c = l >> 4;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      q.q[kk] = (i < cols) ? ld16(qb + i * D + 32 * kk + 8 * c) : u32x4{0, 0, 0, 0};
+  }
+
+  // kb[u]/vb[u]: element offset of row 0 of sub-tile u for this KV head.
+  static __device__ __forceinline__ void load(Buf& b, const Elem* kc, const Elem* vc,
+                                              const int64_t kb[2], int rs) {
+    const int l = lane_id(), i = l & 15, c = l >> 4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) b.k[u][kk] = ld16(kc + kb[u] + i * rs + 32 * kk + 8 * c);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        b.v[u][r] = *reinterpret_cast<const VVec*>(vc + kb[u] + (4 * c + r) * rs + VW * i);
+    }
+  }
+
+  static __device__ __forceinline__ void qk(const Buf& b, const Q& q, f32x4 s[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.k[u][kk]),
+                                                       __builtin_bit_cast(bf16x8, q.q[kk]), s[u], 0,
+                                                       0, 0);
+    }
+  }
+
+  static __device__ __forceinline__ void zero_v_rows(Buf& b, int valid) {
+    const int c = lane_id() >> 4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (16 * u + 4 * c + r >= valid) b.v[u][r] = VVec{};
+  }
+
+  static __device__ __forceinline__ uint32_t pick(const VVec& a, const VVec& b, int t) {
+    const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+    return __builtin_amdgcn_perm(b[t >> 1], a[t >> 1], sel);
+  }
+
+  // O^T[dim tile t] += V^T P^T; k-slot 4u + r of every lane is token 16u + 4c + r.
+  static __device__ __forceinline__ void pv(const Buf& b, const float p[2][4], f32x4 o[NDT]) {
+    bf16x8 pb;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pb[4 * u + r] = (__bf16)p[u][r];
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) {
+      u32x4 a;
+      a[0] = pick(b.v[0][0], b.v[0][1], t);
+      a[1] = pick(b.v[0][2], b.v[0][3], t);
+      a[2] = pick(b.v[1][0], b.v[1][1], t);
+      a[3] = pick(b.v[1][2], b.v[1][3], t);
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pb, o[t], 0, 0, 0);
+    }
+  }
+
+  // Output dim held in o[dt][r] by a lane of row group c.
+  static __device__ __forceinline__ int out_dim(int dt, int c, int r) { return VW * (4 * c + r) + dt; }
+};
+
+// ------------------------------------------------------------------ fp32 tile
+template <int D_, int BS_>
+struct TileF32 {
+  static constexpr int D = D_;
+  static constexpr int BS = BS_;
+  static constexpr bool kDoubleBuffer = false;
+  static constexpr int NQ = D / 16;   // float4 pieces of a row per lane
+  static constexpr int NH = D / 64;   // 64-dim halves of a V row
+  static constexpr int NDT = D / 16;
+  typedef float Elem;
+
+  struct Q { f32x4 q[NQ]; };
+  struct Buf { f32x4 k[2][NQ]; f32x4 v[2][4][NH]; };
+
+  static __device__ __forceinline__ void load_q(Q& q, const Elem* qb, int cols) {
+    const int l = lane_id(), i = l & 15, c = l >> 4;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j)
+      q.q[j] = (i < cols) ? *reinterpret_cast<const f32x4*>(qb + i * D + 16 * j + 4 * c)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  static __device__ __forceinline__ void load(Buf& b, const Elem* kc, const Elem* vc,
+                                              const int64_t kb[2], int rs) {
+    const int l = lane_id(), i = l & 15, c = l >> 4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int j = 0; j < NQ; ++j)
+        b.k[u][j] = *reinterpret_cast<const f32x4*>(kc + kb[u] + i * rs + 16 * j + 4 * c);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf)
+          b.v[u][r][hf] = *reinterpret_cast<const f32x4*>(vc + kb[u] + (4 * c + r) * rs + 64 * hf + 4 * i);
+    }
+  }
+
+  // k-slot c of MFMA (j, e) is dim 16j + 4c + e.
+  static __device__ __forceinline__ void qk(const Buf& b, const Q& q, f32x4 s[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NQ; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(b.k[u][j][e], q.q[j][e], s[u], 0, 0, 0);
+    }
+  }
+
+  static __device__ __forceinline__ void zero_v_rows(Buf& b, int valid) {
+    const int c = lane_id() >> 4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (16 * u + 4 * c + r >= valid)
+#pragma unroll
+          for (int hf = 0; hf < NH; ++hf) b.v[u][r][hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // For token slot (u, r) the k-slot c of every lane is token 16u + 4c + r.
+  static __device__ __forceinline__ void pv(const Buf& b, const float p[2][4], f32x4 o[NDT]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[4 * hf + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(b.v[u][r][hf][e], p[u][r], o[4 * hf + e], 0, 0, 0);
+  }
+
+  static __device__ __forceinline__ int out_dim(int dt, int c, int r) {
+    return 64 * (dt >> 2) + 16 * c + 4 * r + (dt & 3);
+  }
+};
+
+// ------------------------------------------------------------ block id window
+// Lane k of `val` holds the physical id of logical block base + k (clamped to
+// the pool), for the blocks a sequence owns.
+struct BlockWindow {
+  const int32_t* row;
+  int nblk;
+  int base;
+  int val;
+  int64_t max_id;
+
+  __device__ __forceinline__ void fill(int b) {
+    base = b;
+    const int lb = b + lane_id();
+    int v = 0;
+    if (lb < nblk) v = row[lb];
+    v = v < 0 ? 0 : v;
+    val = (int64_t)v > max_id ? (int)max_id : v;
+  }
+  // Physical id of logical block lb (clamped to the sequence's last block).
+  __device__ __forceinline__ int get(int lb) {
+    lb = lb < nblk ? lb : nblk - 1;
+    if (lb - base >= kWave || lb < base) fill(lb);
+    return __builtin_amdgcn_readlane(val, lb - base);
+  }
+};
+
+// One range [c0, c1) of chunks of one pair.
+template <class Tile>
+__device__ __forceinline__ void run_segment(const DecodeArgs& a, int s, int row, int h, int ht, int L,
+                                            int c0, int c1, bool single, int64_t slot) {
+  constexpr int D = Tile::D, BS = Tile::BS, NDT = Tile::NDT;
+  typedef typename Tile::Elem Elem;
+  const int l = lane_id(), col = l & 15, c = l >> 4;
+  const int G = a.group;
+  const int cols = min(16, G - 16 * ht);
+  const int hq0 = h * G + 16 * ht;
+  const int Hkv = a.num_kv_heads;
+  const int rs = Hkv * D;                              // elements between token rows
+  const Elem* kc = reinterpret_cast<const Elem*>(a.key_cache);
+  const Elem* vc = reinterpret_cast<const Elem*>(a.value_cache);
+
+  typename Tile::Q q;
+  Tile::load_q(q, reinterpret_cast<const Elem*>(a.query) + ((int64_t)row * a.num_q_heads + hq0) * D, cols);
+
+  BlockWindow win;
+  win.row = a.block_tables + (int64_t)s * a.max_blocks;
+  win.nblk = (L + BS - 1) / BS;
+  win.max_id = a.num_blocks - 1;
+  win.fill((c0 * 32) / BS);
+
+  auto bases = [&](int ch, int64_t kb[2]) {
+    if (BS == 16) {
+      kb[0] = ((int64_t)win.get(2 * ch) * BS * Hkv + h) * D;
+      kb[1] = ((int64_t)win.get(2 * ch + 1) * BS * Hkv + h) * D;
+    } else {
+      const int64_t b0 = ((int64_t)win.get(ch) * BS * Hkv + h) * D;
+      kb[0] = b0;
+      kb[1] = b0 + (int64_t)16 * rs;
+    }
+  };
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 o[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int last_chunk = (L - 1) >> 5;
+  auto compute = [&](typename Tile::Buf& b, int ch) {
+    f32x4 sc[2];
+    Tile::qk(b, q, sc);
+    const int valid = L - ch * 32;                     // tokens of this chunk inside the sequence
+    const bool tail = (ch == last_chunk) && (valid < 32);
+    if (tail) Tile::zero_v_rows(b, valid);
+    float x[2][4];
+    float cm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = sc[u][r] * a.scale_log2;
+        if (tail && (16 * u + 4 * c + r >= valid)) v = -INFINITY;
+        x[u][r] = v;
+        cm = fmaxf(cm, v);
+      }
+    cm = wave_max_across_rows(cm);
+    const float mn = fmaxf(m, cm);
+    const float alpha = fast_exp2(m - mn);             // 0 on the first chunk (m = -inf)
+    m = mn;
+    float p[2][4];
+    float ps = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[u][r] = fast_exp2(x[u][r] - mn);
+        ps += p[u][r];
+      }
+    lsum = lsum * alpha + ps;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) o[t] *= alpha;
+    Tile::pv(b, p, o);
+  };
+
+  if constexpr (Tile::kDoubleBuffer) {
+    typename Tile::Buf A, B;
+    int64_t kb[2];
+    bases(c0, kb);
+    Tile::load(A, kc, vc, kb, rs);
+    int ch = c0;
+    while (true) {
+      if (ch + 1 < c1) { bases(ch + 1, kb); Tile::load(B, kc, vc, kb, rs); }
+      compute(A, ch);
+      if (++ch >= c1) break;
+      if (ch + 1 < c1) { bases(ch + 1, kb); Tile::load(A, kc, vc, kb, rs); }
+      compute(B, ch);
+      if (++ch >= c1) break;
+    }
+  } else {
+    typename Tile::Buf A;
+    int64_t kb[2];
+    for (int ch = c0; ch < c1; ++ch) {
+      bases(ch, kb);
+      Tile::load(A, kc, vc, kb, rs);
+      compute(A, ch);
+    }
+  }
+
+  lsum = wave_sum_across_rows(lsum);
+  if (col >= cols) return;
+  if (single) {
+    const float inv = 1.f / lsum;
+    float* dst = a.out + ((int64_t)row * a.num_q_heads + hq0 + col) * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int g = 0; g < NDT / 4; ++g)
+        st16f(dst + Tile::out_dim(4 * g, c, r),
+              f32x4{o[4 * g][r] * inv, o[4 * g + 1][r] * inv, o[4 * g + 2][r] * inv, o[4 * g + 3][r] * inv});
+  } else {
+    const int64_t pidx = slot * a.tile_cols + col;
+    float* dst = a.part_o + pidx * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int g = 0; g < NDT / 4; ++g)
+        st16f(dst + Tile::out_dim(4 * g, c, r),
+              f32x4{o[4 * g][r], o[4 * g + 1][r], o[4 * g + 2][r], o[4 * g + 3][r]});
+    if (c == 0) {
+      a.part_ml[2 * pidx] = m;
+      a.part_ml[2 * pidx + 1] = lsum;
+    }
+  }
+}
+
+__device__ __forceinline__ int clamp_len(int L, int max_tok) {
+  return L < 0 ? 0 : (L > max_tok ? max_tok : L);
+}
+
+// Chunks of sequence s that this launch handles (0 for skipped sequences).
+__device__ __forceinline__ int seq_chunks(const DecodeArgs& a, int s, int max_tok) {
+  if (a.qsl != nullptr && a.qsl[s + 1] - a.qsl[s] != 1) return 0;
+  return (clamp_len(a.seq_lens[s], max_tok) + 31) >> 5;
+}
+
+template <class Tile>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+decode_split_kernel(const DecodeArgs a) {
+  extern __shared__ int cum[];                         // [num_seqs + 1]
+  const int B = a.num_seqs;
+  const int max_tok = a.max_blocks * Tile::BS;
+  block_prefix_sum<256>(B, cum, [&](int s) { return seq_chunks(a, s, max_tok); });
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= B; i += 256) a.cum[i] = cum[i];
+
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= a.workers) return;
+  const int ppseq = a.num_kv_heads * a.head_tiles;     // pairs per sequence
+  const int64_t total = (int64_t)ppseq * cum[B];
+  const int64_t x0 = total * w / a.workers;
+  const int64_t x1 = total * (w + 1) / a.workers;
+  if (x0 >= x1) return;
+
+  // sequence holding chunk x0: the last s with ppseq * cum[s] <= x0
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)ppseq * cum[mid] <= x0) lo = mid; else hi = mid;
+  }
+  int s = uniform(lo);
+  int n_s = uniform(cum[s + 1] - cum[s]);
+  const int64_t local = x0 - (int64_t)ppseq * uniform(cum[s]);
+  int pr = (int)(local / n_s);
+  int ch = (int)(local - (int64_t)pr * n_s);
+  int64_t remaining = x1 - x0;
+  while (true) {
+    const int seg = (int)min<int64_t>(n_s - ch, remaining);
+    const int L = uniform(clamp_len(a.seq_lens[s], max_tok));
+    const int row = a.qsl ? uniform(a.qsl[s]) : s;
+    run_segment<Tile>(a, s, row, pr / a.head_tiles, pr % a.head_tiles, L, ch, ch + seg,
+                      ch == 0 && seg == n_s, (int64_t)s * ppseq + pr + w);
+    remaining -= seg;
+    if (remaining <= 0) break;
+    ch = 0;
+    if (++pr == ppseq) {
+      pr = 0;
+      do { ++s; } while (s < B - 1 && cum[s + 1] == cum[s]);
+      if (s >= B) break;
+      s = uniform(s);
+      n_s = uniform(cum[s + 1] - cum[s]);
+    }
+  }
+}
+
+// Merge the parts of one pair (blockIdx.x = s * ppseq + pr); pairs done by a
+// single worker were written by the split kernel, empty sequences get zeros.
+template <int D>
+__global__ void __launch_bounds__(256) decode_reduce_kernel(const DecodeArgs a) {
+  const int ppseq = a.num_kv_heads * a.head_tiles;
+  const int pair = blockIdx.x;
+  const int s = pair / ppseq, pr = pair - s * ppseq;
+  if (a.qsl != nullptr && a.qsl[s + 1] - a.qsl[s] != 1) return;
+  const int h = pr / a.head_tiles, ht = pr - h * a.head_tiles;
+  const int cols = min(16, a.group - 16 * ht);
+  const int hq0 = h * a.group + 16 * ht;
+  const int row = a.qsl ? a.qsl[s] : s;
+  float* out = a.out + ((int64_t)row * a.num_q_heads + hq0) * D;
+  const int B = a.num_seqs;
+  const int n_s = a.cum[s + 1] - a.cum[s];
+  constexpr int Q4 = D / 4;
+  if (n_s == 0) {
+    for (int i = threadIdx.x; i < cols * Q4; i += 256) st16f(out + 4 * i, f32x4{0.f, 0.f, 0.f, 0.f});
+    return;
+  }
+  const int64_t total = (int64_t)ppseq * a.cum[B];
+  const int64_t first = (int64_t)ppseq * a.cum[s] + (int64_t)pr * n_s;
+  const int64_t last = first + n_s - 1;
+  const int64_t W = a.workers;
+  // worker owning chunk x: the last i with floor(i * total / W) <= x
+  const int i0 = (int)(((first + 1) * W - 1) / total);
+  const int i1 = (int)(((last + 1) * W - 1) / total);
+  if (i0 == i1) return;
+  // Workers between i0 and i1 with an empty range (possible when there are
+  // fewer chunks than workers) wrote nothing.
+  auto empty = [&](int k) { return total * k / W == total * (k + 1) / W; };
+  for (int i = threadIdx.x; i < cols * Q4; i += 256) {
+    const int col = i / Q4, d4 = i - col * Q4;
+    float M = -INFINITY;
+    for (int k = i0; k <= i1; ++k)
+      if (!empty(k)) M = fmaxf(M, a.part_ml[2 * (((int64_t)pair + k) * a.tile_cols + col)]);
+    float Z = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k = i0; k <= i1; ++k) {
+      if (empty(k)) continue;
+      const int64_t p = ((int64_t)pair + k) * a.tile_cols + col;
+      const float wk = fast_exp2(a.part_ml[2 * p] - M);
+      Z += wk * a.part_ml[2 * p + 1];
+      acc += wk * *reinterpret_cast<const f32x4*>(a.part_o + p * D + 4 * d4);
+    }
+    st16f(out + col * D + 4 * d4, acc * (1.f / Z));
+  }
+}
+
+size_t decode_workspace_bytes(int num_seqs, int num_kv_heads, int group, int head_dim, int workers) {
+  const int head_tiles = (group + 15) / 16;
+  const int tile_cols = group < 16 ? group : 16;
+  const size_t slots = (size_t)num_seqs * num_kv_heads * head_tiles + (size_t)workers;
+  const size_t cum = ((size_t)(num_seqs + 1) * 4 + 255) / 256 * 256;
+  const size_t ml = (slots * tile_cols * 2 * 4 + 255) / 256 * 256;
+  const size_t o = slots * tile_cols * head_dim * 4;
+  return cum + ml + o;
+}
+
+void decode_workspace_carve(DecodeArgs& a, void* ws, int head_dim) {
+  const size_t slots = (size_t)a.num_seqs * a.num_kv_heads * a.head_tiles + (size_t)a.workers;
+  char* p = static_cast<char*>(ws);
+  a.cum = reinterpret_cast<int*>(p);
+  p += ((size_t)(a.num_seqs + 1) * 4 + 255) / 256 * 256;
+  a.part_ml = reinterpret_cast<float*>(p);
+  p += (slots * a.tile_cols * 2 * 4 + 255) / 256 * 256;
+  a.part_o = reinterpret_cast<float*>(p);
+  (void)head_dim;
+}
+
+template <class Tile>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+  const int grid = (a.workers + 3) / 4;
+  const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int);
+  if (e0) (void)hipEventRecord(e0, stream);
+  hipLaunchKernelGGL(decode_split_kernel<Tile>, dim3(grid), dim3(256), lds, stream, a);
+  if (e1) (void)hipEventRecord(e1, stream);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int pairs = a.num_seqs * a.num_kv_heads * a.head_tiles;
+  if (pairs > 0)
+    hipLaunchKernelGGL(decode_reduce_kernel<Tile::D>, dim3(pairs), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int block_size, bool bf16,
+                         hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+#define PKV_CASE(T, D, BS) \
+  if (head_dim == D && block_size == BS) return launch_decode_t<T<D, BS>>(a, stream, e0, e1);
+  if (bf16) {
+    PKV_CASE(TileBf16, 128, 16)
+    PKV_CASE(TileBf16, 128, 32)
+    PKV_CASE(TileBf16, 64, 16)
+    PKV_CASE(TileBf16, 64, 32)
+  } else {
+    PKV_CASE(TileF32, 128, 16)
+    PKV_CASE(TileF32, 128, 32)
+    PKV_CASE(TileF32, 64, 16)
+    PKV_CASE(TileF32, 64, 32)
+  }
+#undef PKV_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

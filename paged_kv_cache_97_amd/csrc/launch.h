@@ -1,0 +1,53 @@
+// Host-side launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Everything the decode kernels read; built and validated by the API layer.
+struct DecodeArgs {
+  float* out;                 // [B, Hq, D] (decode) or [T, Hq, D] (varlen rows)
+  const void* query;          // [rows, Hq, D]
+  const void* key_cache;      // [NB, BS, Hkv, D]
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  // Optional varlen row offsets [B + 1].  NULL: sequence s owns query/out row s.
+  // Otherwise only sequences with exactly one row (decode rows) are handled,
+  // at row qsl[s]; every other sequence is left untouched.
+  const int32_t* qsl;
+  int max_blocks;
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;                  // Hq / Hkv
+  int head_tiles;             // ceil(group / 16)
+  int tile_cols;              // min(group, 16)
+  int64_t num_blocks;
+  float scale_log2;           // scale * log2(e)
+  int workers;                // wavefronts sharing the work (split points)
+  // workspace
+  int* cum;                   // [B + 1] chunk prefix sums (written by the split kernel)
+  float* part_ml;             // [slots, tile_cols, 2]  (max, sum) in the log2 domain
+  float* part_o;              // [slots, tile_cols, D]  unnormalised partial outputs
+};
+
+size_t decode_workspace_bytes(int num_seqs, int num_kv_heads, int group, int head_dim, int workers);
+// Splits the workspace into the DecodeArgs pointers.
+void decode_workspace_carve(DecodeArgs& a, void* ws, int head_dim);
+
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int block_size, bool bf16,
+                         hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+
+hipError_t launch_slot_mapping(const int32_t* bt, int num_seqs, int max_blocks, const int32_t* pos,
+                               const int32_t* qsl, int num_tokens, int block_size, int64_t* slots,
+                               hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
+                                    const int64_t* slots, int num_tokens, int row_bytes,
+                                    int64_t num_slots, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,252 @@
+"""Python binding of libpagedkv.so (argument marshalling only).
+
+Every function takes torch tensors that already live on the GPU, checks their
+dtype/shape/contiguity, and passes raw device pointers plus the current HIP
+stream to the C ABI declared in include/pagedkv.h.  All compute happens in the
+library's HIP kernels; there is no CPU path.  A missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PKV_F32, PKV_BF16 = 0, 1
+_c_i32, _c_i64, _c_f32, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+_SIGNATURES = {
+    "pkv_version": (_c_i32, []),
+    "pkv_status_string": (ctypes.c_char_p, [_c_i32]),
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_compute_slot_mapping": (_c_i32, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp]),
+    "pkv_reshape_and_cache": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i64,
+                                       _c_i32, _c_i32, _c_vp]),
+    "pkv_decode_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pkv_paged_attention_decode": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32, _c_i32,
+                                            _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_f32, _c_i32, _c_vp,
+                                            _c_sz, _c_vp]),
+    "pkv_varlen_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pkv_paged_attention_varlen": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,
+                                            _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
+                                            _c_f32, _c_i32, _c_vp, _c_sz, _c_vp]),
+    "pkv_set_profile_events": (_c_i32, [_c_vp, _c_vp]),
+    "pkv_set_decode_workers": (_c_i32, [_c_i32]),
+    "pkv_set_waves_per_cu": (_c_i32, [_c_i32]),
+    "pkv_get_waves_per_cu": (_c_i32, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpagedkv.so, building it first only if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build_lib
+            build_lib.build()
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+class PagedKVError(RuntimeError):
+    pass
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        L = lib()
+        raise PagedKVError("%s failed: %s (%s)" % (what, L.pkv_status_string(status).decode(),
+                                                   L.pkv_last_error().decode()))
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got %d" % (name, ndim, t.dim()))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _kv_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    if t.dtype == torch.float32:
+        return PKV_F32
+    raise ValueError("KV dtype must be bfloat16 or float32, got %s" % t.dtype)
+
+
+# ----------------------------------------------------------------- the four calls
+def compute_slot_mapping(block_tables: torch.Tensor, positions: torch.Tensor, query_start_loc: torch.Tensor,
+                         block_size: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """slot[t] = block_tables[s][pos // bs] * bs + pos % bs (int64, -1 for padding)."""
+    B, M = block_tables.shape
+    T = positions.shape[0]
+    if out is None:
+        out = torch.empty(T, dtype=torch.int64, device=positions.device)
+    if query_start_loc.shape[0] != B + 1:
+        raise ValueError("query_start_loc must have num_seqs + 1 entries")
+    _check(lib().pkv_compute_slot_mapping(_dev(block_tables, "block_tables", torch.int32, 2), B, M,
+                                          _dev(positions, "positions", torch.int32, 1),
+                                          _dev(query_start_loc, "query_start_loc", torch.int32, 1), T,
+                                          int(block_size), _dev(out, "slot_mapping", torch.int64, 1),
+                                          _stream(positions)), "compute_slot_mapping")
+    return out
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                      slot_mapping: torch.Tensor) -> None:
+    """Scatter key/value [T, Hkv, D] rows into the [NB, bs, Hkv, D] pools at their slots."""
+    T, Hkv, D = key.shape
+    NB, bs = key_cache.shape[0], key_cache.shape[1]
+    if value.shape != key.shape or value_cache.shape != key_cache.shape or key_cache.shape[2:] != (Hkv, D):
+        raise ValueError("key/value/cache shapes disagree")
+    if key.dtype != key_cache.dtype or value.dtype != key.dtype or value_cache.dtype != key.dtype:
+        raise ValueError("key/value/caches must share one dtype")
+    if slot_mapping.shape[0] != T:
+        raise ValueError("slot_mapping must have one entry per token")
+    _check(lib().pkv_reshape_and_cache(_dev(key, "key", ndim=3), _dev(value, "value", ndim=3),
+                                       _dev(key_cache, "key_cache", ndim=4), _dev(value_cache, "value_cache", ndim=4),
+                                       _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, Hkv, D, NB, bs,
+                                       _kv_dtype(key), _stream(key)), "reshape_and_cache")
+
+
+def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                          dtype: torch.dtype) -> int:
+    return int(lib().pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                               PKV_BF16 if dtype == torch.bfloat16 else PKV_F32))
+
+
+def varlen_workspace_size(num_seqs: int, num_tokens: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          max_query_len: int, block_size: int, dtype: torch.dtype) -> int:
+    return int(lib().pkv_varlen_workspace_size(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                                               max_query_len, block_size,
+                                               PKV_BF16 if dtype == torch.bfloat16 else PKV_F32))
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    # the library checks the size (PKV_EWORKSPACE); this only allocates a default
+    if workspace is None:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def paged_attention_decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                           block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float, max_seq_len: int,
+                           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[s, h] = softmax(scale * q[s, h] K^T) V over seq_lens[s] paged tokens; float32 [B, Hq, D]."""
+    B, Hq, D = query.shape
+    NB, bs, Hkv, Dk = key_cache.shape
+    if Dk != D or value_cache.shape != key_cache.shape:
+        raise ValueError("cache shapes disagree with the query")
+    if query.dtype != key_cache.dtype or value_cache.dtype != key_cache.dtype:
+        raise ValueError("query and caches must share one dtype")
+    if block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_tables/seq_lens must have num_seqs rows")
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=query.device)
+    ws = _workspace(decode_workspace_size(B, Hq, Hkv, D, bs, query.dtype), query.device, workspace)
+    _check(lib().pkv_paged_attention_decode(
+        _dev(out, "out", torch.float32, 3), _dev(query, "query", ndim=3), _dev(key_cache, "key_cache", ndim=4),
+        _dev(value_cache, "value_cache", ndim=4), _dev(block_tables, "block_tables", torch.int32, 2),
+        block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32, 1), B, Hq, Hkv, D, NB, bs,
+        int(max_seq_len), float(scale), _kv_dtype(query), _dev(ws, "workspace"),
+        ws.numel() * ws.element_size(), _stream(query)), "paged_attention_decode")
+    return out
+
+
+def paged_attention_varlen(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                           block_tables: torch.Tensor, seq_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                           scale: float, max_query_len: int, max_seq_len: int, out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Mixed prefill-chunk + decode rows; float32 [T, Hq, D] (bottom-right causal)."""
+    T, Hq, D = query.shape
+    NB, bs, Hkv, Dk = key_cache.shape
+    B = seq_lens.shape[0]
+    if Dk != D or value_cache.shape != key_cache.shape:
+        raise ValueError("cache shapes disagree with the query")
+    if query.dtype != key_cache.dtype or value_cache.dtype != key_cache.dtype:
+        raise ValueError("query and caches must share one dtype")
+    if block_tables.shape[0] != B or query_start_loc.shape[0] != B + 1:
+        raise ValueError("block_tables/query_start_loc do not match seq_lens")
+    if out is None:
+        out = torch.empty(T, Hq, D, dtype=torch.float32, device=query.device)
+    ws = _workspace(varlen_workspace_size(B, T, Hq, Hkv, D, max_query_len, bs, query.dtype), query.device, workspace)
+    _check(lib().pkv_paged_attention_varlen(
+        _dev(out, "out", torch.float32, 3), _dev(query, "query", ndim=3), _dev(key_cache, "key_cache", ndim=4),
+        _dev(value_cache, "value_cache", ndim=4), _dev(block_tables, "block_tables", torch.int32, 2),
+        block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32, 1),
+        _dev(query_start_loc, "query_start_loc", torch.int32, 1), B, T, int(max_query_len), int(max_seq_len),
+        Hq, Hkv, D, NB, bs, float(scale), _kv_dtype(query), _dev(ws, "workspace"),
+        ws.numel() * ws.element_size(), _stream(query)), "paged_attention_varlen")
+    return out
+
+
+# ----------------------------------------------------------------- knobs and timing
+def set_decode_workers(n: int) -> int:
+    return int(lib().pkv_set_decode_workers(int(n)))
+
+
+def set_waves_per_cu(n: int) -> int:
+    return int(lib().pkv_set_waves_per_cu(int(n)))
+
+
+class HipEvent:
+    """A raw hipEvent_t (created through the HIP runtime torch already loaded)."""
+    _rt = None
+
+    @classmethod
+    def _runtime(cls):
+        if cls._rt is None:
+            rt = ctypes.CDLL("libamdhip64.so")
+            rt.hipEventCreate.argtypes = [ctypes.POINTER(_c_vp)]
+            rt.hipEventDestroy.argtypes = [_c_vp]
+            rt.hipEventSynchronize.argtypes = [_c_vp]
+            rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _c_vp, _c_vp]
+            cls._rt = rt
+        return cls._rt
+
+    def __init__(self):
+        h = _c_vp()
+        if self._runtime().hipEventCreate(ctypes.byref(h)) != 0:
+            raise PagedKVError("hipEventCreate failed")
+        self.handle = h
+
+    def __del__(self):
+        try:
+            if self._rt is not None and self.handle:
+                self._rt.hipEventDestroy(self.handle)
+        except Exception:
+            pass
+
+    @staticmethod
+    def elapsed_ms(start: "HipEvent", stop: "HipEvent") -> float:
+        rt = HipEvent._runtime()
+        rt.hipEventSynchronize(stop.handle)
+        ms = ctypes.c_float()
+        if rt.hipEventElapsedTime(ctypes.byref(ms), start.handle, stop.handle) != 0:
+            raise PagedKVError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+
+def set_profile_events(start: Optional[HipEvent], stop: Optional[HipEvent]) -> None:
+    _check(lib().pkv_set_profile_events(start.handle if start else None, stop.handle if stop else None),
+           "set_profile_events")

@@ -1,0 +1,173 @@
+"""GPU parity of slot mapping, cache write and paged decode attention against
+the float64 oracle, through the C ABI.  Needs an MI355X and libpagedkv.so."""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_97_amd import ops
+from paged_kv_cache_97_amd import workloads as W
+from gpu_harness import (assert_attn_close, log, oracle_step, run_step, same_bits, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ops.lib()                     # loud failure when the library is missing
+    return torch.device("cuda:0")
+
+
+def _check_full(wl, dev, label):
+    log("[%s] seed %d: B=%d T=%d NB=%d maxL=%d" % (label, wl.seed, wl.num_seqs, wl.num_tokens, wl.num_blocks,
+                                                   wl.max_seq_len))
+    t = upload(wl, dev)
+    slots, out = run_step(wl, t)
+    r_slots, r_kc, r_vc, r_out = oracle_step(wl)
+    assert np.array_equal(slots.cpu().numpy(), r_slots), "slot mapping differs"
+    assert same_bits(t["key_cache"], r_kc) and same_bits(t["value_cache"], r_vc), "cache contents differ"
+    assert_attn_close(out, r_out, wl.spec.dtype, label)
+    return t, out
+
+
+# ------------------------------------------------------------------ configs at full size
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_config_full_size(cfg, dev):
+    _check_full(W.generate(cfg), dev, "config %d" % cfg)
+
+
+def test_config1_worked_position(dev):
+    """Config 1 writes the new token of sequence 0 at position 35, the pages'
+    worked example position; its slot follows the drawn table."""
+    wl = W.generate(1)
+    t = upload(wl, dev)
+    slots, _ = run_step(wl, t)
+    assert wl.positions[0] == 35
+    assert int(slots[0]) == int(wl.block_tables[0, 2]) * 16 + 3
+
+
+# ------------------------------------------------------------------ reduced shapes, more seeds
+SMALL = {
+    "gqa8-bs16": W.reduced(3, num_decode=24, decode_len=("lognormal", 300.0, W.LOGNORMAL_SIGMA, 1, 1500)),
+    "mha-bf16": W.reduced(2, num_decode=8, decode_len=("uniform", 1, 700)),
+    "gqa4-bs32": W.reduced(4, num_decode=4, decode_len=("uniform", 2100, 4000)),
+    "gqa16-d64": W.reduced(3, num_decode=10, num_q_heads=32, num_kv_heads=2, head_dim=64,
+                           decode_len=("uniform", 1, 900)),
+    "gqa32-d128-bs32": W.reduced(3, num_decode=6, num_q_heads=64, num_kv_heads=2, block_size=32,
+                                 decode_len=("uniform", 30, 700)),
+    "gqa2-d64-bs32": W.reduced(3, num_decode=9, num_q_heads=8, num_kv_heads=4, head_dim=64, block_size=32,
+                               decode_len=("uniform", 1, 400)),
+    "gqa6-odd": W.reduced(3, num_decode=7, num_q_heads=12, num_kv_heads=2, decode_len=("uniform", 1, 300)),
+    "f32-d128": W.reduced(1, num_decode=6, num_q_heads=8, num_kv_heads=2, head_dim=128, pool_blocks=None,
+                          decode_len=("uniform", 1, 300), decode_len_is_ctx=False),
+    "f32-gqa4-bs32": W.reduced(1, num_decode=5, num_q_heads=16, num_kv_heads=4, block_size=32, pool_blocks=None,
+                               decode_len=("uniform", 1, 500), decode_len_is_ctx=False),
+}
+
+
+@pytest.mark.parametrize("seed", [101, 102, 103])
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_reduced_shapes(name, seed, dev):
+    _check_full(W.generate(SMALL[name], seed=seed), dev, name)
+
+
+@pytest.mark.parametrize("workers", [1, 2, 3, 7, 64, 333, 4096])
+def test_forced_split_points(workers, dev):
+    """Every split of the chunk space (1 worker .. many) matches the oracle."""
+    prev = ops.set_decode_workers(workers)
+    try:
+        _check_full(W.generate(SMALL["gqa8-bs16"], seed=7), dev, "workers=%d" % workers)
+        _check_full(W.generate(SMALL["f32-d128"], seed=8), dev, "workers=%d f32" % workers)
+    finally:
+        ops.set_decode_workers(prev)
+
+
+def test_lengths_at_chunk_edges(dev):
+    lens = (1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 1000)
+    spec = W.reduced(3, num_decode=len(lens), decode_len=("fixed", lens))
+    _check_full(W.generate(spec, seed=9), dev, "edges")
+
+
+def test_zero_length_sequence_gives_zero_row(dev):
+    wl = W.generate(SMALL["gqa8-bs16"], seed=10)
+    t = upload(wl, dev)
+    run_step(wl, t)
+    lens = t["seq_lens"].clone()
+    lens[3] = 0
+    lens[5] = 0
+    out = ops.paged_attention_decode(t["query"], t["key_cache"], t["value_cache"], t["block_tables"], lens,
+                                     wl.scale, wl.max_seq_len)
+    full = ops.paged_attention_decode(t["query"], t["key_cache"], t["value_cache"], t["block_tables"],
+                                      t["seq_lens"], wl.scale, wl.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[3]) == 0 and torch.count_nonzero(out[5]) == 0
+    others = [i for i in range(wl.num_seqs) if i not in (3, 5)]
+    assert torch.isfinite(out).all()
+    np.testing.assert_allclose(out[others].cpu().numpy(), full[others].cpu().numpy(), rtol=0, atol=2e-2)
+
+
+def test_block_permutation_is_bitwise_invariant(dev):
+    """Moving every physical block and renaming the table entries changes no
+    output bit: the reduction order depends only on logical positions."""
+    wl = W.generate(SMALL["gqa8-bs16"], seed=11)
+    t = upload(wl, dev)
+    _, out = run_step(wl, t)
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(wl.num_blocks)).to(dev)
+    kc2 = torch.empty_like(t["key_cache"])
+    vc2 = torch.empty_like(t["value_cache"])
+    kc2[perm] = t["key_cache"]
+    vc2[perm] = t["value_cache"]
+    bt = t["block_tables"].long()
+    bt2 = torch.where(bt >= 0, perm[bt.clamp(min=0)], bt).int()
+    out2 = ops.paged_attention_decode(t["query"], kc2, vc2, bt2, t["seq_lens"], wl.scale, wl.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
+
+
+def test_shared_prefix_equals_private_copies_bitwise(dev):
+    wl = W.generate(SMALL["gqa4-bs32"], seed=12)
+    t = upload(wl, dev)
+    _, out = run_step(wl, t)
+    nb = wl.spec.shared_prefix_tokens // wl.spec.block_size
+    shared = t["block_tables"][0, :nb].long()
+    extra = (wl.num_seqs - 1) * nb
+    kc2 = torch.cat([t["key_cache"], t["key_cache"][shared].repeat(wl.num_seqs - 1, 1, 1, 1)])
+    vc2 = torch.cat([t["value_cache"], t["value_cache"][shared].repeat(wl.num_seqs - 1, 1, 1, 1)])
+    bt2 = t["block_tables"].clone()
+    new_ids = torch.arange(wl.num_blocks, wl.num_blocks + extra, device=dev, dtype=torch.int32)
+    bt2[1:, :nb] = new_ids.view(wl.num_seqs - 1, nb)
+    out2 = ops.paged_attention_decode(t["query"], kc2, vc2, bt2, t["seq_lens"], wl.scale, wl.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
+
+
+def test_closed_form_uniform_keys_give_mean_of_values(dev):
+    """K = 0 makes every weight equal: the output is the mean of the visible
+    V rows, which also catches a dropped or extra token."""
+    wl = W.generate(SMALL["gqa8-bs16"], seed=13)
+    t = upload(wl, dev)
+    run_step(wl, t)
+    kc = torch.zeros_like(t["key_cache"])
+    out = ops.paged_attention_decode(t["query"], kc, t["value_cache"], t["block_tables"], t["seq_lens"],
+                                     wl.scale, wl.max_seq_len)
+    torch.cuda.synchronize()
+    vc = t["value_cache"].float().cpu()
+    bs, G = wl.spec.block_size, wl.spec.num_q_heads // wl.spec.num_kv_heads
+    for s in range(wl.num_seqs):
+        L = int(wl.seq_lens[s])
+        rows = [vc[int(wl.block_tables[s, p // bs]), p % bs] for p in range(L)]
+        mean = torch.stack(rows).double().mean(0)                      # [Hkv, D]
+        ref = mean.repeat_interleave(G, 0)
+        assert torch.allclose(out[s].double().cpu(), ref, atol=1e-2, rtol=0)
+
+
+def test_rejects_bad_arguments(dev):
+    wl = W.generate(1)
+    t = upload(wl, dev)
+    with pytest.raises(ops.PagedKVError, match="EUNSUPPORTED"):
+        ops.paged_attention_decode(t["query"][:, :, :48].contiguous(), t["key_cache"][..., :48].contiguous(),
+                                   t["value_cache"][..., :48].contiguous(), t["block_tables"], t["seq_lens"],
+                                   0.1, 40)
+    with pytest.raises(ops.PagedKVError, match="EWORKSPACE"):
+        ops.paged_attention_decode(t["query"], t["key_cache"], t["value_cache"], t["block_tables"],
+                                   t["seq_lens"], 0.1, 40, workspace=torch.empty(256, dtype=torch.uint8, device=dev))
