@@ -30,6 +30,74 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "paged-attn decode KV GB/s (% of MI355X HBM peak); seq-tokens/s per step"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_traffic.json")
+KERNEL_SOURCES = ["paged_kv_cache_97_amd/csrc/decode_kernels.hip", "paged_kv_cache_97_amd/csrc/common.h",
+                  "paged_kv_cache_97_amd/csrc/launch.h"]
+CALIB_BYTES = 256 << 20
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _load_traffic():
+    """Counter-measured HBM bytes per launch of the split kernel, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec
+
+
+def summarize(fetch_dir: str, write_dir: str, kv_bytes: int, cmd: str) -> dict:
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of each kernel, calibrated by
+    the same counters on a plain device copy of CALIB_BYTES."""
+    import csv
+    import glob
+
+    def read(d, counter):
+        rows = []
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                rows += [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        return rows
+
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = read(d, counter)
+        calib = [float(r["Counter_Value"]) for r in rows
+                 if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= 65536]
+        if not calib:
+            raise SystemExit("no calibration copy found in %s" % d)
+        factor = (CALIB_BYTES / 1024.0) / (sum(calib) / len(calib))
+        per = {}
+        for r in rows:
+            name = r["Kernel_Name"]
+            per.setdefault(name, []).append(float(r["Counter_Value"]))
+        out[counter] = {"calibration_factor": factor,
+                        "kernels": {k: {"dispatches": len(v), "raw_kib_mean": sum(v) / len(v),
+                                        "bytes_per_launch": sum(v) / len(v) * 1024.0 * factor}
+                                    for k, v in per.items()}}
+    split = [k for k in out["FETCH_SIZE"]["kernels"] if "decode_split_kernel" in k]
+    rec = {"source_hash": kernel_source_hash(), "command": cmd, "algorithmic_kv_bytes": kv_bytes,
+           "counters": out}
+    if split:
+        fb = out["FETCH_SIZE"]["kernels"][split[0]]["bytes_per_launch"]
+        wb = out["WRITE_SIZE"]["kernels"].get(split[0], {}).get("bytes_per_launch", 0.0)
+        rec["split_kernel"] = split[0]
+        rec["traffic_bytes_per_launch"] = fb + wb
+        rec["fetch_bytes_per_launch"] = fb
+        rec["write_bytes_per_launch"] = wb
+    return rec
 
 
 def _cpu_baseline(wl, budget_s: float = 12.0):
@@ -66,7 +134,21 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="run warmup + steps untimed, then one plain %d MiB device copy (counter runs)" % (CALIB_BYTES >> 20))
+    ap.add_argument("--summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs of --kernels-only into %s" % os.path.relpath(TRAFFIC_FILE, ROOT))
+    ap.add_argument("--command", default="", help="command line recorded with --summarize")
     args = ap.parse_args()
+    if args.summarize:
+        from paged_kv_cache_97_amd import workloads as W
+        wl = W.generate(args.config)
+        rec = summarize(args.summarize[0], args.summarize[1], wl.kv_bytes_logical(), args.command)
+        os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps({k: v for k, v in rec.items() if k != "counters"}))
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU only: the hot path runs on a single MI355X and this build has "
               "no multi-GPU path (requested --gpus %d)" % args.gpus, file=sys.stderr)
@@ -105,6 +187,17 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.kernels_only:
+        for _ in range(args.steps):
+            step()
+        a = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print("bench: kernels-only pass done (%d steps, calibration copy %d bytes)" % (args.steps, CALIB_BYTES),
+              file=sys.stderr, flush=True)
+        return 0
 
     evs = [(ops.HipEvent(), ops.HipEvent()) for _ in range(args.steps)]
     t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -126,6 +219,8 @@ def main() -> int:
     print("bench: %.4f ms/step, split kernel mean %.4f ms (min %.4f, p90 %.4f)" % (
         ms_step, k_mean, float(np.min(kern_ms)), float(np.percentile(kern_ms, 90))), file=sys.stderr, flush=True)
 
+    tr = _load_traffic() if args.config == 3 else None
+    traffic = round(tr["traffic_bytes_per_launch"]) if tr else None
     cpu = None
     if not args.no_cpu:
         cpu = _cpu_baseline(wl)
@@ -143,7 +238,7 @@ def main() -> int:
         "kv_tokens_per_s": round(float(wl.seq_lens.sum()) / (ms_step * 1e-3), 1),
         "roofline": {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel_ms_mean": round(k_mean, 5), "bytes_per_launch": kv_bytes},
+                     "traffic": traffic, "kernel_ms_mean": round(k_mean, 5), "bytes_per_launch": kv_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

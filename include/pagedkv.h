@@ -189,7 +189,7 @@ int pkv_paged_attention_varlen(float* out, const void* query, const void* key_ca
  * different split points.  Returns the previous value.
  *
  * pkv_set_waves_per_cu: default worker density per compute unit (4..16,
- * multiple of 4; default 8).  Returns the previous value.
+ * multiple of 4; default 4).  Returns the previous value.
  */
 int pkv_set_profile_events(void* start_event, void* stop_event);
 int pkv_set_decode_workers(int32_t workers);

@@ -16,7 +16,7 @@ thread_local char g_err[512] = "";
 thread_local hipEvent_t g_ev_start = nullptr;
 thread_local hipEvent_t g_ev_stop = nullptr;
 std::atomic<int> g_workers_override{0};
-std::atomic<int> g_waves_per_cu{8};
+std::atomic<int> g_waves_per_cu{4};
 
 constexpr int kMaxSeqs = 8192;
 

@@ -15,21 +15,27 @@
 
 namespace pkv {
 
+// query_start_loc is staged in LDS when it fits (lds_n > 0), so the owner
+// search costs one global round trip instead of log2(num_seqs).
 __global__ void __launch_bounds__(256)
 slot_mapping_kernel(const int32_t* __restrict__ block_tables, int num_seqs, int max_blocks,
                     const int32_t* __restrict__ positions, const int32_t* __restrict__ qsl,
-                    int num_tokens, int block_size, int64_t* __restrict__ slots) {
+                    int num_tokens, int block_size, int64_t* __restrict__ slots, int lds_n) {
+  extern __shared__ int qs[];
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  for (int i = threadIdx.x; i < lds_n; i += blockDim.x) qs[i] = qsl[i];
+  if (lds_n > 0) __syncthreads();
   if (t >= num_tokens) return;
+  const int p = positions[t];
+  const int32_t* q = lds_n > 0 ? qs : qsl;
   // sequence owning row t: the last s with qsl[s] <= t
   int lo = 0, hi = num_seqs;  // invariant: qsl[lo] <= t (qsl[0] == 0), answer in [lo, hi)
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (qsl[mid] <= t) lo = mid; else hi = mid;
+    if (q[mid] <= t) lo = mid; else hi = mid;
   }
   int64_t slot = -1;
-  const int p = positions[t];
-  if (num_seqs > 0 && t < qsl[lo + 1] && p >= 0) {
+  if (num_seqs > 0 && t < q[lo + 1] && p >= 0) {
     const int lb = p / block_size;
     if (lb < max_blocks) {
       const int phys = block_tables[(int64_t)lo * max_blocks + lb];
@@ -64,8 +70,9 @@ hipError_t launch_slot_mapping(const int32_t* bt, int num_seqs, int max_blocks, 
                                hipStream_t stream) {
   const int threads = 256;
   const int blocks = (num_tokens + threads - 1) / threads;
-  hipLaunchKernelGGL(slot_mapping_kernel, dim3(blocks), dim3(threads), 0, stream, bt, num_seqs,
-                     max_blocks, pos, qsl, num_tokens, block_size, slots);
+  const int lds_n = num_seqs + 1 <= 8192 ? num_seqs + 1 : 0;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(blocks), dim3(threads), (size_t)lds_n * sizeof(int), stream,
+                     bt, num_seqs, max_blocks, pos, qsl, num_tokens, block_size, slots, lds_n);
   return hipGetLastError();
 }
 

@@ -34,9 +34,15 @@
 //    reduced across the four 16-lane rows with two cross-lane xors; the sum
 //    stays lane-local until the end.  Masked tokens are excluded by select
 //    and their V rows zeroed, so stale NaN slots never reach a product.
+//  * KV tiles are read once per step, so they are loaded non-temporally
+//    (streaming hint): on MI355X this lifts the split kernel from about 5.2
+//    to 5.8 TB/s on the 128-sequence GQA batch, close to the ~6 TB/s a plain
+//    random 4 KB-tile gather reaches on the same part.
 //  * Block ids: each wave holds a 64-entry window of its block-table row in
 //    one VGPR and reads entries with v_readlane; loads of chunk n+1 are in
 //    flight while chunk n is computed (bf16).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -54,6 +60,7 @@ struct TileBf16 {
   static constexpr int D = D_;
   static constexpr int BS = BS_;
   static constexpr bool kDoubleBuffer = true;
+  static constexpr int kWavesPerEU = 2;
   static constexpr int KK = D / 32;   // K=32 slices of the QK contraction
   static constexpr int VW = D / 16;   // dims per lane of a V row (= O^T dim tiles)
   static constexpr int NDT = D / 16;
@@ -71,17 +78,26 @@ struct TileBf16 {
       q.q[kk] = (i < cols) ? ld16(qb + i * D + 32 * kk + 8 * c) : u32x4{0, 0, 0, 0};
   }
 
-  // kb[u]/vb[u]: element offset of row 0 of sub-tile u for this KV head.
-  static __device__ __forceinline__ void load(Buf& b, const Elem* kc, const Elem* vc,
-                                              const int64_t kb[2], int rs) {
-    const int l = lane_id(), i = l & 15, c = l >> 4;
+  // Per-lane element offsets inside a sub-tile (row 0 of the tile at the
+  // uniform base pointer): K row i, dims 8c..; V rows 4c + r, dims VW*i...
+  static __device__ __forceinline__ int k_lane_off(int rs) {
+    const int l = lane_id();
+    return (l & 15) * rs + 8 * (l >> 4);
+  }
+  static __device__ __forceinline__ int v_lane_off(int rs) {
+    const int l = lane_id();
+    return 4 * (l >> 4) * rs + VW * (l & 15);
+  }
+
+  // kp[u]/vp[u]: wave-uniform pointers to row 0 of sub-tile u for this KV head.
+  static __device__ __forceinline__ void load(Buf& b, const Elem* const kp[2], const Elem* const vp[2],
+                                              int koff, int voff, int rs) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) b.k[u][kk] = ld16(kc + kb[u] + i * rs + 32 * kk + 8 * c);
+      for (int kk = 0; kk < KK; ++kk) b.k[u][kk] = ld_stream(kp[u] + koff + 32 * kk);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        b.v[u][r] = *reinterpret_cast<const VVec*>(vc + kb[u] + (4 * c + r) * rs + VW * i);
+      for (int r = 0; r < 4; ++r) b.v[u][r] = ld_stream_v<VVec>(vp[u] + voff + r * rs);
     }
   }
 
@@ -139,6 +155,7 @@ struct TileF32 {
   static constexpr int D = D_;
   static constexpr int BS = BS_;
   static constexpr bool kDoubleBuffer = false;
+  static constexpr int kWavesPerEU = D == 128 ? 1 : 2;  // fp32 D=128 needs > 256 VGPRs
   static constexpr int NQ = D / 16;   // float4 pieces of a row per lane
   static constexpr int NH = D / 64;   // 64-dim halves of a V row
   static constexpr int NDT = D / 16;
@@ -155,19 +172,25 @@ struct TileF32 {
                           : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  static __device__ __forceinline__ void load(Buf& b, const Elem* kc, const Elem* vc,
-                                              const int64_t kb[2], int rs) {
-    const int l = lane_id(), i = l & 15, c = l >> 4;
+  static __device__ __forceinline__ int k_lane_off(int rs) {
+    const int l = lane_id();
+    return (l & 15) * rs + 4 * (l >> 4);
+  }
+  static __device__ __forceinline__ int v_lane_off(int rs) {
+    const int l = lane_id();
+    return 4 * (l >> 4) * rs + 4 * (l & 15);
+  }
+
+  static __device__ __forceinline__ void load(Buf& b, const Elem* const kp[2], const Elem* const vp[2],
+                                              int koff, int voff, int rs) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int j = 0; j < NQ; ++j)
-        b.k[u][j] = *reinterpret_cast<const f32x4*>(kc + kb[u] + i * rs + 16 * j + 4 * c);
+      for (int j = 0; j < NQ; ++j) b.k[u][j] = ld_stream_v<f32x4>(kp[u] + koff + 16 * j);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int hf = 0; hf < NH; ++hf)
-          b.v[u][r][hf] = *reinterpret_cast<const f32x4*>(vc + kb[u] + (4 * c + r) * rs + 64 * hf + 4 * i);
+        for (int hf = 0; hf < NH; ++hf) b.v[u][r][hf] = ld_stream_v<f32x4>(vp[u] + voff + r * rs + 64 * hf);
     }
   }
 
@@ -263,15 +286,22 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, int s, int row,
   win.max_id = a.num_blocks - 1;
   win.fill((c0 * 32) / BS);
 
-  auto bases = [&](int ch, int64_t kb[2]) {
+  const int koff = Tile::k_lane_off(rs);
+  const int voff = Tile::v_lane_off(rs);
+  // Wave-uniform pointers to row 0 of the two 16-token sub-tiles of chunk ch.
+  auto bases = [&](int ch, const Elem* kp[2], const Elem* vp[2]) {
+    int64_t b0, b1;
     if (BS == 16) {
-      kb[0] = ((int64_t)win.get(2 * ch) * BS * Hkv + h) * D;
-      kb[1] = ((int64_t)win.get(2 * ch + 1) * BS * Hkv + h) * D;
+      b0 = ((int64_t)win.get(2 * ch) * BS * Hkv + h) * D;
+      b1 = ((int64_t)win.get(2 * ch + 1) * BS * Hkv + h) * D;
     } else {
-      const int64_t b0 = ((int64_t)win.get(ch) * BS * Hkv + h) * D;
-      kb[0] = b0;
-      kb[1] = b0 + (int64_t)16 * rs;
+      b0 = ((int64_t)win.get(ch) * BS * Hkv + h) * D;
+      b1 = b0 + (int64_t)16 * rs;
     }
+    kp[0] = kc + b0;
+    kp[1] = kc + b1;
+    vp[0] = vc + b0;
+    vp[1] = vc + b1;
   };
 
   float m = -INFINITY, lsum = 0.f;
@@ -279,13 +309,14 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, int s, int row,
 #pragma unroll
   for (int t = 0; t < NDT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int last_chunk = (L - 1) >> 5;
-  auto compute = [&](typename Tile::Buf& b, int ch) {
+  // One chunk of the online softmax.  TAIL: the chunk holds the sequence's
+  // last `valid` (< 32) tokens; the others are masked by select and their V
+  // rows zeroed so stale slot contents never reach a product.
+  auto compute = [&](typename Tile::Buf& b, auto tail_tag, int valid) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
     f32x4 sc[2];
     Tile::qk(b, q, sc);
-    const int valid = L - ch * 32;                     // tokens of this chunk inside the sequence
-    const bool tail = (ch == last_chunk) && (valid < 32);
-    if (tail) Tile::zero_v_rows(b, valid);
+    if constexpr (TAIL) Tile::zero_v_rows(b, valid);
     float x[2][4];
     float cm = -INFINITY;
 #pragma unroll
@@ -293,7 +324,7 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, int s, int row,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v = sc[u][r] * a.scale_log2;
-        if (tail && (16 * u + 4 * c + r >= valid)) v = -INFINITY;
+        if constexpr (TAIL) v = (16 * u + 4 * c + r < valid) ? v : -INFINITY;
         x[u][r] = v;
         cm = fmaxf(cm, v);
       }
@@ -315,29 +346,54 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, int s, int row,
     for (int t = 0; t < NDT; ++t) o[t] *= alpha;
     Tile::pv(b, p, o);
   };
+  // The last chunk of a range may be the sequence's partial chunk.
+  auto compute_last = [&](typename Tile::Buf& b, int ch) {
+    const int valid = uniform(L - ch * 32);
+    if (valid < 32) compute(b, std::true_type{}, valid);
+    else compute(b, std::false_type{}, 32);
+  };
 
+  const Elem* kp[2];
+  const Elem* vp[2];
   if constexpr (Tile::kDoubleBuffer) {
+    // Steady state: the loads of chunk ch+1 are always in flight while chunk
+    // ch is computed (unconditional prefetch keeps the wait counts exact).
     typename Tile::Buf A, B;
-    int64_t kb[2];
-    bases(c0, kb);
-    Tile::load(A, kc, vc, kb, rs);
+    bases(c0, kp, vp);
+    Tile::load(A, kp, vp, koff, voff, rs);
     int ch = c0;
-    while (true) {
-      if (ch + 1 < c1) { bases(ch + 1, kb); Tile::load(B, kc, vc, kb, rs); }
-      compute(A, ch);
-      if (++ch >= c1) break;
-      if (ch + 1 < c1) { bases(ch + 1, kb); Tile::load(A, kc, vc, kb, rs); }
-      compute(B, ch);
-      if (++ch >= c1) break;
+    // sched_barrier keeps the compiler from sinking the prefetch below the
+    // waits of the chunk being computed.
+    while (ch + 2 < c1) {
+      bases(ch + 1, kp, vp);
+      Tile::load(B, kp, vp, koff, voff, rs);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(A, std::false_type{}, 32);
+      bases(ch + 2, kp, vp);
+      Tile::load(A, kp, vp, koff, voff, rs);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(B, std::false_type{}, 32);
+      ch += 2;
+    }
+    if (ch + 1 < c1) {
+      bases(ch + 1, kp, vp);
+      Tile::load(B, kp, vp, koff, voff, rs);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(A, std::false_type{}, 32);
+      compute_last(B, ch + 1);
+    } else {
+      compute_last(A, ch);
     }
   } else {
     typename Tile::Buf A;
-    int64_t kb[2];
-    for (int ch = c0; ch < c1; ++ch) {
-      bases(ch, kb);
-      Tile::load(A, kc, vc, kb, rs);
-      compute(A, ch);
+    for (int ch = c0; ch < c1 - 1; ++ch) {
+      bases(ch, kp, vp);
+      Tile::load(A, kp, vp, koff, voff, rs);
+      compute(A, std::false_type{}, 32);
     }
+    bases(c1 - 1, kp, vp);
+    Tile::load(A, kp, vp, koff, voff, rs);
+    compute_last(A, c1 - 1);
   }
 
   lsum = wave_sum_across_rows(lsum);
@@ -378,7 +434,7 @@ __device__ __forceinline__ int seq_chunks(const DecodeArgs& a, int s, int max_to
 }
 
 template <class Tile>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Tile::kWavesPerEU)))
 decode_split_kernel(const DecodeArgs a) {
   extern __shared__ int cum[];                         // [num_seqs + 1]
   const int B = a.num_seqs;
@@ -459,17 +515,20 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(const DecodeArgs a) 
   auto empty = [&](int k) { return total * k / W == total * (k + 1) / W; };
   for (int i = threadIdx.x; i < cols * Q4; i += 256) {
     const int col = i / Q4, d4 = i - col * Q4;
-    float M = -INFINITY;
-    for (int k = i0; k <= i1; ++k)
-      if (!empty(k)) M = fmaxf(M, a.part_ml[2 * (((int64_t)pair + k) * a.tile_cols + col)]);
-    float Z = 0.f;
+    // one pass with a running maximum: rescale what has been merged so far
+    float M = -INFINITY, Z = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int k = i0; k <= i1; ++k) {
       if (empty(k)) continue;
       const int64_t p = ((int64_t)pair + k) * a.tile_cols + col;
-      const float wk = fast_exp2(a.part_ml[2 * p] - M);
-      Z += wk * a.part_ml[2 * p + 1];
-      acc += wk * *reinterpret_cast<const f32x4*>(a.part_o + p * D + 4 * d4);
+      const float mk = a.part_ml[2 * p], lk = a.part_ml[2 * p + 1];
+      const f32x4 ok = *reinterpret_cast<const f32x4*>(a.part_o + p * D + 4 * d4);
+      const float mn = fmaxf(M, mk);
+      const float s_old = fast_exp2(M - mn), s_new = fast_exp2(mk - mn);
+      Z = Z * s_old + lk * s_new;
+      acc = acc * s_old + ok * s_new;
+      M = mn;
     }
     st16f(out + col * D + 4 * d4, acc * (1.f / Z));
   }
