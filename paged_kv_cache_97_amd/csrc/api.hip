@@ -242,11 +242,62 @@ int pkv_paged_attention_varlen(float* out, const void* query, const void* key_ca
                                int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
                                int32_t block_size, float scale, pkv_dtype dtype, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  (void)out; (void)query; (void)key_cache; (void)value_cache; (void)block_tables; (void)max_blocks_per_seq;
-  (void)seq_lens; (void)query_start_loc; (void)num_seqs; (void)num_tokens; (void)max_query_len;
-  (void)max_seq_len; (void)num_q_heads; (void)num_kv_heads; (void)head_dim; (void)num_blocks;
-  (void)block_size; (void)scale; (void)dtype; (void)workspace; (void)workspace_bytes; (void)stream;
-  return fail(PKV_EUNSUPPORTED, "varlen attention is not built yet");
+  int st = check_shape(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_seqs > kMaxSeqs) return fail(PKV_EUNSUPPORTED, "num_seqs %d (max %d)", num_seqs, kMaxSeqs);
+  if (num_tokens < 0 || max_query_len < 0 || max_blocks_per_seq < 0 || num_blocks < 0 || max_seq_len < 0)
+    return fail(PKV_EINVAL, "negative size");
+  if (num_tokens > 0 && max_query_len == 0) return fail(PKV_EINVAL, "max_query_len is 0 with %d tokens", num_tokens);
+  if (num_seqs == 0 || num_tokens == 0) return ok();
+  if (!out || !query || !seq_lens || !query_start_loc ||
+      (max_blocks_per_seq > 0 && (!block_tables || !key_cache || !value_cache)))
+    return fail(PKV_EINVAL, "null pointer");
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PKV_EINVAL, "out/query/cache pointers must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale is not finite");
+  if (max_blocks_per_seq > 0 && num_blocks == 0) return fail(PKV_EINVAL, "empty pool with a non-empty block table");
+  const int group = num_q_heads / num_kv_heads;
+  if ((int64_t)max_query_len * group > (int64_t)1 << 30) return fail(PKV_EUNSUPPORTED, "max_query_len too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  {
+    // check the workspace before enqueueing anything
+    const size_t need = pkv::decode_workspace_bytes(num_seqs, num_kv_heads, group, head_dim, decode_workers());
+    if (!workspace || workspace_bytes < need)
+      return fail(PKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
+  }
+  if (g_ev_start) (void)hipEventRecord(g_ev_start, s);
+  if (max_query_len > 1) {
+    pkv::PrefillArgs p{};
+    p.out = out;
+    p.query = query;
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.block_tables = block_tables;
+    p.seq_lens = seq_lens;
+    p.qsl = query_start_loc;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = group;
+    p.num_blocks = num_blocks;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    int cus = current_cus();
+    p.waves = (cus > 0 ? cus : 256) * 4;
+    hipError_t e = pkv::launch_prefill(p, head_dim, block_size, dtype == PKV_BF16, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  }
+  // decode rows (sequences with exactly one query row) through the split kernels;
+  // the profile events (if any) were recorded around the whole call's main kernels
+  hipEvent_t e0 = g_ev_start, e1 = g_ev_stop;
+  g_ev_start = nullptr;
+  int rc = run_decode(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens,
+                      query_start_loc, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                      max_seq_len, scale, dtype, workspace, workspace_bytes, s);
+  g_ev_start = e0;
+  g_ev_stop = e1;
+  return rc;
 }
 
 }  // extern "C"

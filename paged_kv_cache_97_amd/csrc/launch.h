@@ -51,3 +51,28 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc
                                     int64_t num_slots, hipStream_t stream);
 
 }  // namespace pkv
+
+namespace pkv {
+
+// Prefill-chunk rows of a varlen step (sequences with more than one query row).
+struct PrefillArgs {
+  float* out;                 // [T, Hq, D]
+  const void* query;          // [T, Hq, D]
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* qsl;         // [B + 1]
+  int max_blocks;
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;
+  int64_t num_blocks;
+  float scale_log2;
+  int waves;                  // wavefronts in the grid
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool bf16, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,243 @@
+// MFMA tile primitives shared by the decode and varlen kernels (gfx950).
+//
+// A "chunk" is 32 consecutive logical tokens of one KV head, held as two
+// 16-token sub-tiles.  With tokens on the M side of the MFMA tiles:
+//   S^T[token, col] = K[token, :] . Q[col, :]          (A operand = K rows)
+//   O^T[dim, col]  += V^T[dim, token] P^T[token, col]   (A operand = V rows)
+// so a lane owns column col = lane % 16 of every accumulator, and the S^T
+// accumulator's values are already the P^T operand's k-slots.
+#pragma once
+
+#include "common.h"
+
+namespace pkv {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int N> struct U32Vec;
+template <> struct U32Vec<2> { typedef u32x2 type; };
+template <> struct U32Vec<4> { typedef u32x4 type; };
+
+// ------------------------------------------------------------------ bf16 tile
+template <int D_, int BS_>
+struct TileBf16 {
+  static constexpr int D = D_;
+  static constexpr int BS = BS_;
+  static constexpr bool kDoubleBuffer = true;
+  static constexpr int kWavesPerEU = 2;
+  static constexpr int KK = D / 32;   // K=32 slices of the QK contraction
+  static constexpr int VW = D / 16;   // dims per lane of a V row (= O^T dim tiles)
+  static constexpr int NDT = D / 16;
+  typedef uint16_t Elem;
+  typedef typename U32Vec<VW / 2>::type VVec;
+
+  struct Q { u32x4 q[KK]; };
+  struct Buf { u32x4 k[2][KK]; VVec v[2][4]; };
+
+  // Query head `i` (lane % 16) of the tile, slice kk: dims 32kk + 8c .. +7.
+  static __device__ __forceinline__ void load_q(Q& q, const Elem* qb, int cols) {
+    const int l = lane_id(), i = l & 15, c = l >> 4;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      q.q[kk] = (i < cols) ? ld16(qb + i * D + 32 * kk + 8 * c) : u32x4{0, 0, 0, 0};
+  }
+
+  // Column given by a per-lane pointer to its query row (zeros when !valid).
+  static __device__ __forceinline__ void load_q_col(Q& q, const Elem* colp, bool valid) {
+    const int c = lane_id() >> 4;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) q.q[kk] = valid ? ld16(colp + 32 * kk + 8 * c) : u32x4{0, 0, 0, 0};
+  }
+
+  // Per-lane element offsets inside a sub-tile (row 0 of the tile at the
+  // uniform base pointer): K row i, dims 8c..; V rows 4c + r, dims VW*i...
+  static __device__ __forceinline__ int k_lane_off(int rs) {
+    const int l = lane_id();
+    return (l & 15) * rs + 8 * (l >> 4);
+  }
+  static __device__ __forceinline__ int v_lane_off(int rs) {
+    const int l = lane_id();
+    return 4 * (l >> 4) * rs + VW * (l & 15);
+  }
+
+  // kp[u]/vp[u]: wave-uniform pointers to row 0 of sub-tile u for this KV head.
+  static __device__ __forceinline__ void load(Buf& b, const Elem* const kp[2], const Elem* const vp[2],
+                                              int koff, int voff, int rs) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) b.k[u][kk] = ld_stream(kp[u] + koff + 32 * kk);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b.v[u][r] = ld_stream_v<VVec>(vp[u] + voff + r * rs);
+    }
+  }
+
+  static __device__ __forceinline__ void qk(const Buf& b, const Q& q, f32x4 s[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.k[u][kk]),
+                                                       __builtin_bit_cast(bf16x8, q.q[kk]), s[u], 0,
+                                                       0, 0);
+    }
+  }
+
+  static __device__ __forceinline__ void zero_v_rows(Buf& b, int valid) {
+    const int c = lane_id() >> 4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (16 * u + 4 * c + r >= valid) b.v[u][r] = VVec{};
+  }
+
+  static __device__ __forceinline__ uint32_t pick(const VVec& a, const VVec& b, int t) {
+    const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+    return __builtin_amdgcn_perm(b[t >> 1], a[t >> 1], sel);
+  }
+
+  // O^T[dim tile t] += V^T P^T; k-slot 4u + r of every lane is token 16u + 4c + r.
+  static __device__ __forceinline__ void pv(const Buf& b, const float p[2][4], f32x4 o[NDT]) {
+    bf16x8 pb;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pb[4 * u + r] = (__bf16)p[u][r];
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) {
+      u32x4 a;
+      a[0] = pick(b.v[0][0], b.v[0][1], t);
+      a[1] = pick(b.v[0][2], b.v[0][3], t);
+      a[2] = pick(b.v[1][0], b.v[1][1], t);
+      a[3] = pick(b.v[1][2], b.v[1][3], t);
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pb, o[t], 0, 0, 0);
+    }
+  }
+
+  // Output dim held in o[dt][r] by a lane of row group c.
+  static __device__ __forceinline__ int out_dim(int dt, int c, int r) { return VW * (4 * c + r) + dt; }
+};
+
+// ------------------------------------------------------------------ fp32 tile
+template <int D_, int BS_>
+struct TileF32 {
+  static constexpr int D = D_;
+  static constexpr int BS = BS_;
+  static constexpr bool kDoubleBuffer = false;
+  static constexpr int kWavesPerEU = D == 128 ? 1 : 2;  // fp32 D=128 needs > 256 VGPRs
+  static constexpr int NQ = D / 16;   // float4 pieces of a row per lane
+  static constexpr int NH = D / 64;   // 64-dim halves of a V row
+  static constexpr int NDT = D / 16;
+  typedef float Elem;
+
+  struct Q { f32x4 q[NQ]; };
+  struct Buf { f32x4 k[2][NQ]; f32x4 v[2][4][NH]; };
+
+  static __device__ __forceinline__ void load_q(Q& q, const Elem* qb, int cols) {
+    const int l = lane_id(), i = l & 15, c = l >> 4;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j)
+      q.q[j] = (i < cols) ? *reinterpret_cast<const f32x4*>(qb + i * D + 16 * j + 4 * c)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  static __device__ __forceinline__ void load_q_col(Q& q, const Elem* colp, bool valid) {
+    const int c = lane_id() >> 4;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j)
+      q.q[j] = valid ? *reinterpret_cast<const f32x4*>(colp + 16 * j + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  static __device__ __forceinline__ int k_lane_off(int rs) {
+    const int l = lane_id();
+    return (l & 15) * rs + 4 * (l >> 4);
+  }
+  static __device__ __forceinline__ int v_lane_off(int rs) {
+    const int l = lane_id();
+    return 4 * (l >> 4) * rs + 4 * (l & 15);
+  }
+
+  static __device__ __forceinline__ void load(Buf& b, const Elem* const kp[2], const Elem* const vp[2],
+                                              int koff, int voff, int rs) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) b.k[u][j] = ld_stream_v<f32x4>(kp[u] + koff + 16 * j);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) b.v[u][r][hf] = ld_stream_v<f32x4>(vp[u] + voff + r * rs + 64 * hf);
+    }
+  }
+
+  // k-slot c of MFMA (j, e) is dim 16j + 4c + e.
+  static __device__ __forceinline__ void qk(const Buf& b, const Q& q, f32x4 s[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NQ; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(b.k[u][j][e], q.q[j][e], s[u], 0, 0, 0);
+    }
+  }
+
+  static __device__ __forceinline__ void zero_v_rows(Buf& b, int valid) {
+    const int c = lane_id() >> 4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (16 * u + 4 * c + r >= valid)
+#pragma unroll
+          for (int hf = 0; hf < NH; ++hf) b.v[u][r][hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // For token slot (u, r) the k-slot c of every lane is token 16u + 4c + r.
+  static __device__ __forceinline__ void pv(const Buf& b, const float p[2][4], f32x4 o[NDT]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[4 * hf + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(b.v[u][r][hf][e], p[u][r], o[4 * hf + e], 0, 0, 0);
+  }
+
+  static __device__ __forceinline__ int out_dim(int dt, int c, int r) {
+    return 64 * (dt >> 2) + 16 * c + 4 * r + (dt & 3);
+  }
+};
+
+// ------------------------------------------------------------ block id window
+// Lane k of `val` holds the physical id of logical block base + k (clamped to
+// the pool), for the blocks a sequence owns.
+struct BlockWindow {
+  const int32_t* row;
+  int nblk;
+  int base;
+  int val;
+  int64_t max_id;
+
+  __device__ __forceinline__ void fill(int b) {
+    base = b;
+    const int lb = b + lane_id();
+    int v = 0;
+    if (lb < nblk) v = row[lb];
+    v = v < 0 ? 0 : v;
+    val = (int64_t)v > max_id ? (int)max_id : v;
+  }
+  // Physical id of logical block lb (clamped to the sequence's last block).
+  __device__ __forceinline__ int get(int lb) {
+    lb = lb < nblk ? lb : nblk - 1;
+    if (lb - base >= kWave || lb < base) fill(lb);
+    return __builtin_amdgcn_readlane(val, lb - base);
+  }
+};
+
+}  // namespace pkv

@@ -58,7 +58,7 @@ class WorkloadSpec:
     decode_len_is_ctx: bool = False            # True: the drawn value is ctx, L = ctx + 1
     # prefill chunks: q new tokens after a drawn context
     num_prefill: int = 0
-    prefill_chunk: int = 512
+    prefill_chunk: object = 512                # rows per prefill chunk (int, or one per prefill)
     prefill_ctx: Tuple = ("uniform", 0, 8192)
     prefill_first: bool = True
     # pool
@@ -191,7 +191,10 @@ def generate(cfg, seed: Optional[int] = None, keep_logical: bool = False) -> Wor
     dec = _draw_lengths(rng, spec.decode_len, spec.num_decode)
     dec_ctx = dec if spec.decode_len_is_ctx else dec - 1
     pre_ctx = _draw_lengths(rng, spec.prefill_ctx, spec.num_prefill)
-    pre = [(int(c), spec.prefill_chunk, True) for c in pre_ctx]
+    chunks = spec.prefill_chunk if isinstance(spec.prefill_chunk, tuple) else (spec.prefill_chunk,) * spec.num_prefill
+    if len(chunks) != spec.num_prefill:
+        raise ValueError("prefill_chunk needs one length per prefill")
+    pre = [(int(c), int(q), True) for c, q in zip(pre_ctx, chunks)]
     dcd = [(int(c), 1, False) for c in dec_ctx]
     seqs = pre + dcd if spec.prefill_first else dcd + pre
     B = len(seqs)

@@ -1,0 +1,148 @@
+"""GPU parity of the varlen (chunked prefill + decode) step against the
+float64 oracle, through the C ABI.  Needs an MI355X and libpagedkv.so."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_97_amd import ops
+from paged_kv_cache_97_amd import workloads as W
+from gpu_harness import (assert_attn_close, log, oracle_step, run_step, same_bits, to_dev, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ops.lib()
+    return torch.device("cuda:0")
+
+
+def _check(wl, dev, label):
+    log("[%s] seed %d: B=%d T=%d NB=%d maxL=%d maxq=%d" % (label, wl.seed, wl.num_seqs, wl.num_tokens,
+                                                           wl.num_blocks, wl.max_seq_len, wl.max_query_len))
+    t = upload(wl, dev)
+    slots, out = run_step(wl, t, decode=False)
+    r_slots, r_kc, r_vc, r_out = oracle_step(wl, decode=False)
+    assert np.array_equal(slots.cpu().numpy(), r_slots), "slot mapping differs"
+    assert same_bits(t["key_cache"], r_kc) and same_bits(t["value_cache"], r_vc), "cache contents differ"
+    assert_attn_close(out, r_out, wl.spec.dtype, label)
+    return t, out
+
+
+def test_config5_full_size(dev):
+    _check(W.generate(5), dev, "config 5")
+
+
+def _mixed(**kw):
+    base = dict(num_decode=6, num_prefill=3, prefill_chunk=70, prefill_ctx=("uniform", 0, 300),
+                decode_len=("lognormal", 200.0, W.LOGNORMAL_SIGMA, 16, 600))
+    base.update(kw)
+    return W.reduced(5, **base)
+
+
+SMALL = {
+    "gqa8-bs16": _mixed(),
+    "gqa8-pure-prefill": _mixed(num_decode=0, num_prefill=4, prefill_chunk=33, prefill_ctx=("uniform", 0, 0)),
+    "gqa8-long-chunk": _mixed(num_decode=3, num_prefill=2, prefill_chunk=300, prefill_ctx=("uniform", 0, 900)),
+    "mha-d128": _mixed(num_q_heads=8, num_kv_heads=8, prefill_chunk=37),
+    "gqa4-bs32": _mixed(num_q_heads=16, num_kv_heads=4, block_size=32, prefill_chunk=48),
+    "gqa16-d64": _mixed(num_q_heads=32, num_kv_heads=2, head_dim=64, prefill_chunk=21),
+    "gqa2-d64-bs32": _mixed(num_q_heads=8, num_kv_heads=4, head_dim=64, block_size=32, prefill_chunk=64),
+    "gqa6-odd": _mixed(num_q_heads=12, num_kv_heads=2, prefill_chunk=11),
+    "gqa32": _mixed(num_q_heads=64, num_kv_heads=2, prefill_chunk=9),
+    "decode-first": _mixed(prefill_first=False),
+    "f32-d64": _mixed(dtype="f32", num_q_heads=4, num_kv_heads=4, head_dim=64, prefill_chunk=40),
+    "f32-gqa4-d128": _mixed(dtype="f32", num_q_heads=16, num_kv_heads=4, prefill_chunk=29),
+}
+
+
+@pytest.mark.parametrize("seed", [101, 102])
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_reduced_shapes(name, seed, dev):
+    _check(W.generate(SMALL[name], seed=seed), dev, name)
+
+
+def test_mixed_batch_of_the_page_example(dev, golden):
+    """Two decode rows plus prefills of 50 and 30 rows: 82 rows, 4 requests."""
+    ex = golden["mixed_batch"]
+    spec = W.reduced(5, num_q_heads=16, num_kv_heads=4, num_decode=2, num_prefill=2, prefill_chunk=(50, 30),
+                     prefill_ctx=("fixed", (0, 0)), decode_len=("fixed", (40, 70)), prefill_first=False)
+    wl = W.generate(spec, seed=7)
+    assert wl.num_tokens == ex["total_tokens"] and wl.num_seqs == ex["batch_size"]
+    assert wl.query_start_loc.tolist() == [0, 1, 2, 52, 82]
+    _check(wl, dev, "page-example")
+
+
+def test_decode_rows_equal_decode_call_bitwise(dev):
+    wl = W.generate(SMALL["gqa8-bs16"], seed=21)
+    t = upload(wl, dev)
+    _, out = run_step(wl, t, decode=False)
+    dec = np.where(~wl.is_prefill)[0]
+    rows = torch.from_numpy(wl.query_start_loc[dec].astype(np.int64)).to(dev)
+    idx = torch.from_numpy(dec.astype(np.int64)).to(dev)
+    ref = ops.paged_attention_decode(t["query"][rows].contiguous(), t["key_cache"], t["value_cache"],
+                                     t["block_tables"][idx].contiguous(), t["seq_lens"][idx].contiguous(),
+                                     wl.scale, wl.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(out[rows].view(torch.int32), ref.view(torch.int32))
+
+
+def test_chunked_prefill_equals_one_pass(dev):
+    """A 256-token prompt as 4 chunks of 64 (each written before its
+    attention) matches one pass over the whole prompt."""
+    rng = np.random.default_rng(31)
+    N, Hq, Hkv, D, bs = 256, 16, 4, 128, 16
+    bits = lambda shape: W._to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    q, k, v = bits((N, Hq, D)), bits((N, Hkv, D)), bits((N, Hkv, D))
+    NB = 40
+    table = rng.permutation(NB)[: N // bs].astype(np.int32)[None]
+    kc = torch.full((NB, bs, Hkv, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    vc = kc.clone()
+    bt = torch.from_numpy(table).to(dev)
+    qd, kd, vd = to_dev(q, "bf16", dev), to_dev(k, "bf16", dev), to_dev(v, "bf16", dev)
+    scale = D ** -0.5
+    rows = []
+    for c in range(4):
+        lo, hi = 64 * c, 64 * (c + 1)
+        pos = torch.arange(lo, hi, dtype=torch.int32, device=dev)
+        qsl = torch.tensor([0, 64], dtype=torch.int32, device=dev)
+        sl = ops.compute_slot_mapping(bt, pos, qsl, bs)
+        ops.reshape_and_cache(kd[lo:hi].contiguous(), vd[lo:hi].contiguous(), kc, vc, sl)
+        rows.append(ops.paged_attention_varlen(qd[lo:hi].contiguous(), kc, vc, bt,
+                                               torch.tensor([hi], dtype=torch.int32, device=dev), qsl, scale, 64, hi))
+    one = ops.paged_attention_varlen(qd, kc, vc, bt, torch.tensor([N], dtype=torch.int32, device=dev),
+                                     torch.tensor([0, N], dtype=torch.int32, device=dev), scale, N, N)
+    torch.cuda.synchronize()
+    chunked = torch.cat(rows)
+    # both against the oracle, and against each other
+    kc_h = kc.cpu().view(torch.int16).numpy().view(np.uint16)
+    vc_h = vc.cpu().view(torch.int16).numpy().view(np.uint16)
+    ref = oracle.varlen_attention(q, kc_h, vc_h, table, np.array([N]), np.array([0, N]), scale, "bf16")
+    assert_attn_close(one, ref, "bf16", "one pass")
+    assert_attn_close(chunked, ref, "bf16", "chunked")
+    assert (one - chunked).abs().max().item() <= 2e-2
+
+
+def test_sequence_order_moves_rows(dev):
+    wl = W.generate(SMALL["gqa8-bs16"], seed=41)
+    t = upload(wl, dev)
+    _, out = run_step(wl, t, decode=False)
+    order = np.arange(wl.num_seqs)[::-1].copy()
+    qlen = wl.query_lens[order]
+    qsl2 = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
+    src = np.concatenate([np.arange(wl.query_start_loc[s], wl.query_start_loc[s + 1]) for s in order])
+    src_t = torch.from_numpy(src.astype(np.int64)).to(dev)
+    o_t = torch.from_numpy(order.astype(np.int64)).to(dev)
+    out2 = ops.paged_attention_varlen(t["query"][src_t].contiguous(), t["key_cache"], t["value_cache"],
+                                      t["block_tables"][o_t].contiguous(), t["seq_lens"][o_t].contiguous(),
+                                      torch.from_numpy(qsl2).to(dev), wl.scale, wl.max_query_len, wl.max_seq_len)
+    torch.cuda.synchronize()
+    for i, s in enumerate(order):
+        a = out2[qsl2[i]:qsl2[i + 1]]
+        b = out[wl.query_start_loc[s]:wl.query_start_loc[s + 1]]
+        if wl.is_prefill[s]:
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+        else:
+            assert (a - b).abs().max().item() <= 2e-2
