@@ -18,13 +18,11 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-// Streaming (non-temporal) loads for data read once per kernel.
-__device__ __forceinline__ u32x4 ld_stream(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-template <typename V>
-__device__ __forceinline__ V ld_stream_v(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+// Vector load; STREAM = non-temporal (data read once per kernel).
+template <typename V, bool STREAM>
+__device__ __forceinline__ V ld_v(const void* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+  else return *reinterpret_cast<const V*>(p);
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void st16f(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }

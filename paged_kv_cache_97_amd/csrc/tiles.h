@@ -61,14 +61,17 @@ struct TileBf16 {
   }
 
   // kp[u]/vp[u]: wave-uniform pointers to row 0 of sub-tile u for this KV head.
+  // STREAM: non-temporal loads, for tiles read once per kernel (decode);
+  // tiles that many wavefronts re-read (prefill) use ordinary cached loads.
+  template <bool STREAM = true>
   static __device__ __forceinline__ void load(Buf& b, const Elem* const kp[2], const Elem* const vp[2],
                                               int koff, int voff, int rs) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) b.k[u][kk] = ld_stream(kp[u] + koff + 32 * kk);
+      for (int kk = 0; kk < KK; ++kk) b.k[u][kk] = ld_v<u32x4, STREAM>(kp[u] + koff + 32 * kk);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) b.v[u][r] = ld_stream_v<VVec>(vp[u] + voff + r * rs);
+      for (int r = 0; r < 4; ++r) b.v[u][r] = ld_v<VVec, STREAM>(vp[u] + voff + r * rs);
     }
   }
 
@@ -159,16 +162,17 @@ struct TileF32 {
     return 4 * (l >> 4) * rs + 4 * (l & 15);
   }
 
+  template <bool STREAM = true>
   static __device__ __forceinline__ void load(Buf& b, const Elem* const kp[2], const Elem* const vp[2],
                                               int koff, int voff, int rs) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int j = 0; j < NQ; ++j) b.k[u][j] = ld_stream_v<f32x4>(kp[u] + koff + 16 * j);
+      for (int j = 0; j < NQ; ++j) b.k[u][j] = ld_v<f32x4, STREAM>(kp[u] + koff + 16 * j);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int hf = 0; hf < NH; ++hf) b.v[u][r][hf] = ld_stream_v<f32x4>(vp[u] + voff + r * rs + 64 * hf);
+        for (int hf = 0; hf < NH; ++hf) b.v[u][r][hf] = ld_v<f32x4, STREAM>(vp[u] + voff + r * rs + 64 * hf);
     }
   }
 

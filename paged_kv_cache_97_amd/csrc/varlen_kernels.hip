@@ -47,7 +47,14 @@ prefill_kernel(const PrefillArgs a) {
   const int koff = Tile::k_lane_off(rs);
   const int voff = Tile::v_lane_off(rs);
 
-  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < total; item += a.waves) {
+  // Workgroups are dispatched round-robin over the XCDs (j -> XCD j % 8).
+  // Renumber them XCD-major so consecutive items -- the column blocks of one
+  // (sequence, KV head), which stream the same K/V -- share one XCD's L2.
+  constexpr int kXcds = 8;
+  const int nwg = gridDim.x;
+  int wg = blockIdx.x;
+  if (nwg % kXcds == 0) wg = (blockIdx.x % kXcds) * (nwg / kXcds) + blockIdx.x / kXcds;
+  for (int item = wg * 4 + (threadIdx.x >> 6); item < total; item += a.waves) {
     int lo = 0, hi = B;                                // last s with cum[s] <= item
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -161,22 +168,22 @@ prefill_kernel(const PrefillArgs a) {
     if constexpr (Tile::kDoubleBuffer) {
       typename Tile::Buf A, Bf;
       bases(0, kp, vp);
-      Tile::load(A, kp, vp, koff, voff, rs);
+      Tile::template load<false>(A, kp, vp, koff, voff, rs);
       int ch = 0;
       while (ch + 2 < nch) {
         bases(ch + 1, kp, vp);
-        Tile::load(Bf, kp, vp, koff, voff, rs);
+        Tile::template load<false>(Bf, kp, vp, koff, voff, rs);
         __builtin_amdgcn_sched_barrier(0);
         compute_any(A, ch);
         bases(ch + 2, kp, vp);
-        Tile::load(A, kp, vp, koff, voff, rs);
+        Tile::template load<false>(A, kp, vp, koff, voff, rs);
         __builtin_amdgcn_sched_barrier(0);
         compute_any(Bf, ch + 1);
         ch += 2;
       }
       if (ch + 1 < nch) {
         bases(ch + 1, kp, vp);
-        Tile::load(Bf, kp, vp, koff, voff, rs);
+        Tile::template load<false>(Bf, kp, vp, koff, voff, rs);
         __builtin_amdgcn_sched_barrier(0);
         compute_any(A, ch);
         compute_any(Bf, ch + 1);
@@ -187,7 +194,7 @@ prefill_kernel(const PrefillArgs a) {
       typename Tile::Buf A;
       for (int ch = 0; ch < nch; ++ch) {
         bases(ch, kp, vp);
-        Tile::load(A, kp, vp, koff, voff, rs);
+        Tile::template load<false>(A, kp, vp, koff, voff, rs);
         compute_any(A, ch);
       }
     }
