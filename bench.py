@@ -7,6 +7,9 @@ A step is one decode iteration of the 128-sequence GQA workload (64 query /
 median 1500 clipped to [16, 8192]): slot mapping of the step's new tokens ->
 reshape_and_cache -> paged decode attention (split kernel + merge kernel).
 Inputs are resident in HBM before timing starts.  Prints one JSON line.
+--config N runs another seeded workload the same way (1-4 decode; 5 is the
+mixed chunked-prefill + decode step, timed through the varlen call, whose
+dominant kernel is the MFMA-bound prefill kernel).
 
 value = KV bytes read per step / step time (GB/s, 1 GB = 1e9 B), where KV
 bytes = sum(seq_len) * 2 (K and V) * num_kv_heads * head_dim * 2 B -- each
@@ -31,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0
 METRIC = "paged-attn decode KV GB/s (% of MI355X HBM peak); seq-tokens/s per step"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_97_amd/csrc/decode_kernels.hip", "paged_kv_cache_97_amd/csrc/common.h",
@@ -102,9 +106,22 @@ def summarize(fetch_dir: str, write_dir: str, kv_bytes: int, cmd: str) -> dict:
     return rec
 
 
+def prefill_flops(wl) -> int:
+    """Multiply-add flops of the unmasked (query row, key) pairs of prefill
+    rows: 2 (QK) + 2 (PV) per head and dim."""
+    sp = wl.spec
+    total = 0
+    for s in np.where(wl.is_prefill)[0]:
+        q = int(wl.query_lens[s])
+        ctx = int(wl.seq_lens[s]) - q
+        total += (q * ctx + q * (q + 1) // 2) * 4 * sp.num_q_heads * sp.head_dim
+    return total
+
+
 def _cpu_baseline(wl, budget_s: float = 12.0):
-    """Time the oracle's decode attention on the first sequences of the batch
-    until about budget_s of work is done; report KV GB/s of that sample."""
+    """Time the oracle's attention on the batch's sequences, one at a time in
+    batch order, until about budget_s of work is done; report the KV GB/s of
+    that sample (the same bytes model as the GPU value)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -113,20 +130,29 @@ def _cpu_baseline(wl, budget_s: float = 12.0):
         threads = 1
     slots = oracle.slot_mapping(wl.block_tables, wl.positions, wl.query_start_loc, wl.spec.block_size)
     kc, vc = oracle.reshape_and_cache(wl.key, wl.value, wl.key_cache, wl.value_cache, slots)
+    decode = not wl.is_prefill.any()
     t0 = time.perf_counter()
-    done, tokens = 0, 0
+    done, tokens, rows = 0, 0, 0
     while done < wl.num_seqs and time.perf_counter() - t0 < budget_s:
         s = slice(done, done + 1)
-        oracle.decode_attention(wl.query[s], kc, vc, wl.block_tables[s], wl.seq_lens[s], wl.scale, wl.spec.dtype)
+        r0, r1 = int(wl.query_start_loc[done]), int(wl.query_start_loc[done + 1])
+        if decode:
+            oracle.decode_attention(wl.query[r0:r1], kc, vc, wl.block_tables[s], wl.seq_lens[s], wl.scale,
+                                    wl.spec.dtype)
+        else:
+            oracle.varlen_attention(wl.query[r0:r1], kc, vc, wl.block_tables[s], wl.seq_lens[s],
+                                    np.array([0, r1 - r0]), wl.scale, wl.spec.dtype)
         tokens += int(wl.seq_lens[done])
+        rows += r1 - r0
         done += 1
     dt = time.perf_counter() - t0
     sp = wl.spec
     nbytes = tokens * 2 * sp.num_kv_heads * sp.head_dim * wl.elem_bytes
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": "float64 NumPy oracle decode attention over the first %d of %d sequences "
-                      "(%d KV tokens), %.1f s" % (done, wl.num_seqs, tokens, dt),
-            "seq_tokens_per_s": round(done / dt, 3)}
+            "sample": "float64 NumPy oracle %s attention over the first %d of %d sequences "
+                      "(%d query rows, %d KV tokens), %.1f s" % ("decode" if decode else "varlen", done,
+                                                                wl.num_seqs, rows, tokens, dt),
+            "seq_tokens_per_s": round(rows / dt, 3)}
 
 
 def main() -> int:
@@ -176,15 +202,21 @@ def main() -> int:
     kc, vc = up(wl.key_cache), up(wl.value_cache)
     bt, sl, pos, qsl = up(wl.block_tables), up(wl.seq_lens), up(wl.positions), up(wl.query_start_loc)
     slots = torch.empty(wl.num_tokens, dtype=torch.int64, device=dev)
-    out = torch.empty(wl.num_seqs, sp.num_q_heads, sp.head_dim, dtype=torch.float32, device=dev)
-    ws = torch.empty(ops.decode_workspace_size(wl.num_seqs, sp.num_q_heads, sp.num_kv_heads, sp.head_dim,
-                                               sp.block_size, q.dtype), dtype=torch.uint8, device=dev)
+    out = torch.empty(wl.num_tokens, sp.num_q_heads, sp.head_dim, dtype=torch.float32, device=dev)
+    varlen = bool(wl.is_prefill.any())
+    ws = torch.empty(ops.varlen_workspace_size(wl.num_seqs, wl.num_tokens, sp.num_q_heads, sp.num_kv_heads,
+                                               sp.head_dim, wl.max_query_len, sp.block_size, q.dtype),
+                     dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step():
         ops.compute_slot_mapping(bt, pos, qsl, sp.block_size, out=slots)
         ops.reshape_and_cache(key, value, kc, vc, slots)
-        ops.paged_attention_decode(q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, out=out, workspace=ws)
+        if varlen:
+            ops.paged_attention_varlen(q, kc, vc, bt, sl, qsl, wl.scale, wl.max_query_len, wl.max_seq_len,
+                                       out=out, workspace=ws)
+        else:
+            ops.paged_attention_decode(q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, out=out, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -212,8 +244,9 @@ def main() -> int:
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_stop)
     # Region B: the same K steps again, now with HIP events that the library
-    # records on its stream right before and after the split kernel, giving
-    # that kernel's duration per launch.
+    # records on its stream right before and after the dominant kernel (split
+    # kernel for decode, prefill kernel for varlen), giving its duration per
+    # launch.
     evs = [(ops.HipEvent(), ops.HipEvent()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for e0, e1 in evs:
@@ -226,12 +259,25 @@ def main() -> int:
     kv_bytes = wl.kv_bytes_logical()
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     k_mean = float(np.mean(kern_ms))
-    achieved = kv_bytes / (k_mean * 1e-3) / 1e9
-    print("bench: %.4f ms/step, split kernel mean %.4f ms (min %.4f, p90 %.4f)" % (
-        ms_step, k_mean, float(np.min(kern_ms)), float(np.percentile(kern_ms, 90))), file=sys.stderr, flush=True)
-
-    tr = _load_traffic() if args.config == 3 else None
-    traffic = round(tr["traffic_bytes_per_launch"]) if tr else None
+    kname = "prefill_kernel" if varlen else "decode_split_kernel"
+    print("bench: %.4f ms/step, %s mean %.4f ms (min %.4f, p90 %.4f)" % (
+        ms_step, kname, k_mean, float(np.min(kern_ms)), float(np.percentile(kern_ms, 90))),
+        file=sys.stderr, flush=True)
+    if varlen:
+        flops = prefill_flops(wl)
+        achieved = flops / (k_mean * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 2), "peak": MFMA_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_TFLOPS, 4), "traffic": None,
+                "kernel_ms_mean": round(k_mean, 5), "kernel_ms_min": round(float(np.min(kern_ms)), 5),
+                "flops_per_launch": flops}
+    else:
+        achieved = kv_bytes / (k_mean * 1e-3) / 1e9
+        tr = _load_traffic() if args.config == 3 else None
+        roof = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": round(tr["traffic_bytes_per_launch"]) if tr else None,
+                "kernel_ms_mean": round(k_mean, 5), "kernel_ms_min": round(float(np.min(kern_ms)), 5),
+                "bytes_per_launch": kv_bytes}
     cpu = None
     if not args.no_cpu:
         cpu = _cpu_baseline(wl)
@@ -243,14 +289,11 @@ def main() -> int:
         "config": {"workload": sp.name, "num_seqs": wl.num_seqs, "num_q_heads": sp.num_q_heads,
                    "num_kv_heads": sp.num_kv_heads, "head_dim": sp.head_dim, "block_size": sp.block_size,
                    "sum_seq_len": int(wl.seq_lens.sum()), "max_seq_len": wl.max_seq_len, "seed": wl.seed,
-                   "step": "slot_mapping + reshape_and_cache + paged_attention_decode"},
+                   "step": "slot_mapping + reshape_and_cache + paged_attention_%s" % ("varlen" if varlen else "decode")},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "seq_tokens_per_s": round(wl.num_tokens / (ms_step * 1e-3), 1),
         "kv_tokens_per_s": round(float(wl.seq_lens.sum()) / (ms_step * 1e-3), 1),
-        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": round(achieved, 2),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel_ms_mean": round(k_mean, 5),
-                     "kernel_ms_min": round(float(np.min(kern_ms)), 5), "bytes_per_launch": kv_bytes},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -179,9 +179,11 @@ int pkv_paged_attention_varlen(float* out, const void* query, const void* key_ca
  * Measurement and test knobs (process-wide; not needed for normal use).
  *
  * pkv_set_profile_events: when both are non-NULL, every later attention call
- * on this thread records `start` (a hipEvent_t) right before its main
- * attention kernel and `stop` right after it, on the call's stream, so a
- * caller can time that kernel alone.  NULL, NULL turns it off.
+ * on this thread records `start` (a hipEvent_t) right before its dominant
+ * kernel and `stop` right after it, on the call's stream, so a caller can
+ * time that kernel alone: the split kernel of pkv_paged_attention_decode,
+ * the prefill-chunk kernel of pkv_paged_attention_varlen.  NULL, NULL turns
+ * it off.
  *
  * pkv_set_decode_workers: number of workers (wavefronts) the decode split
  * uses; 0 restores the default (compute units x pkv_get_waves_per_cu()).

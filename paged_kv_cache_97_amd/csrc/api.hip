@@ -266,6 +266,7 @@ int pkv_paged_attention_varlen(float* out, const void* query, const void* key_ca
       return fail(PKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
   }
+  // profile events (if set) bracket the prefill kernel, the step's dominant one
   if (g_ev_start) (void)hipEventRecord(g_ev_start, s);
   if (max_query_len > 1) {
     pkv::PrefillArgs p{};
@@ -288,10 +289,11 @@ int pkv_paged_attention_varlen(float* out, const void* query, const void* key_ca
     hipError_t e = pkv::launch_prefill(p, head_dim, block_size, dtype == PKV_BF16, s);
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
   }
-  // decode rows (sequences with exactly one query row) through the split kernels;
-  // the profile events (if any) were recorded around the whole call's main kernels
+  if (g_ev_stop) (void)hipEventRecord(g_ev_stop, s);
+  // decode rows (sequences with exactly one query row) through the split kernels
   hipEvent_t e0 = g_ev_start, e1 = g_ev_stop;
   g_ev_start = nullptr;
+  g_ev_stop = nullptr;
   int rc = run_decode(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens,
                       query_start_loc, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
                       max_seq_len, scale, dtype, workspace, workspace_bytes, s);
