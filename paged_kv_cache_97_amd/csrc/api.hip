@@ -226,12 +226,20 @@ int pkv_paged_attention_decode(float* out, const void* query, const void* key_ca
                     scale, dtype, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
+static size_t varlen_decode_part(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+  const size_t d = pkv::decode_workspace_bytes(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim,
+                                               decode_workers());
+  return (d + 255) / 256 * 256;
+}
+
 size_t pkv_varlen_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
                                  int32_t block_size, pkv_dtype dtype) {
   (void)num_tokens;
   (void)max_query_len;
-  return pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (num_seqs < 0 || num_seqs > kMaxSeqs) return 0;
+  if (check_shape(num_q_heads, num_kv_heads, head_dim, block_size, dtype) != PKV_OK) return 0;
+  return varlen_decode_part(num_seqs, num_q_heads, num_kv_heads, head_dim) + pkv::prefill_plan_bytes(num_seqs);
 }
 
 int pkv_paged_attention_varlen(float* out, const void* query, const void* key_cache,
@@ -259,9 +267,10 @@ int pkv_paged_attention_varlen(float* out, const void* query, const void* key_ca
   const int group = num_q_heads / num_kv_heads;
   if ((int64_t)max_query_len * group > (int64_t)1 << 30) return fail(PKV_EUNSUPPORTED, "max_query_len too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t dec_bytes = varlen_decode_part(num_seqs, num_q_heads, num_kv_heads, head_dim);
   {
     // check the workspace before enqueueing anything
-    const size_t need = pkv::decode_workspace_bytes(num_seqs, num_kv_heads, group, head_dim, decode_workers());
+    const size_t need = dec_bytes + pkv::prefill_plan_bytes(num_seqs);
     if (!workspace || workspace_bytes < need)
       return fail(PKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
@@ -284,9 +293,10 @@ int pkv_paged_attention_varlen(float* out, const void* query, const void* key_ca
     p.group = group;
     p.num_blocks = num_blocks;
     p.scale_log2 = scale * 1.4426950408889634f;
-    int cus = current_cus();
+    const int cus = current_cus();
     p.waves = (cus > 0 ? cus : 256) * 4;
-    hipError_t e = pkv::launch_prefill(p, head_dim, block_size, dtype == PKV_BF16, s);
+    p.plan = reinterpret_cast<int*>(static_cast<char*>(workspace) + dec_bytes);
+    hipError_t e = pkv::launch_prefill(p, head_dim, block_size, dtype == PKV_BF16, cus, s);
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
   }
   if (g_ev_stop) (void)hipEventRecord(g_ev_stop, s);

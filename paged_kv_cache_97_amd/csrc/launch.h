@@ -71,8 +71,16 @@ struct PrefillArgs {
   int64_t num_blocks;
   float scale_log2;
   int waves;                  // wavefronts in the grid
+  int* plan;                  // workspace: item plan + work counter (prefill_plan_bytes)
 };
 
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool bf16, hipStream_t stream);
+// Workspace bytes of the prefill item plan for num_seqs sequences.
+size_t prefill_plan_bytes(int num_seqs);
+
+// Dispatches to the workgroup-shared kernel (bf16, head_dim 128; plan kernel
+// first) or the per-wave kernel (other shapes).
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool bf16, int cus,
+                          hipStream_t stream);
+hipError_t launch_prefill_lds(const PrefillArgs& a, int block_size, int cus, hipStream_t stream);
 
 }  // namespace pkv

@@ -1,0 +1,352 @@
+// Prefill-chunk rows for bf16, head_dim 128: the workgroup-shared variant.
+//
+// Same computation as prefill_kernel (gaoleia.github.io "PagedAttention 和
+// Continuous Batching" §2.4-§2.5: a chunk of q rows after c cached tokens,
+// row i attends keys 0 .. c + i), organised for the MFMA rate of gfx950:
+//  * a workgroup of 8 waves (two per SIMD, so one wave's MFMAs overlap the
+//    other's softmax) owns an item of 256 (row, head) columns of one
+//    (sequence, KV head); each 32-token K/V chunk is loaded once per
+//    workgroup (coalesced 1 KB rows) into a double-buffered, XOR-swizzled LDS
+//    tile and read by all 8 waves, each computing 2 tiles of 16 columns;
+//  * the O^T accumulators stay in the accumulation registers: the softmax
+//    reference maximum is only moved when a column's maximum grows by more
+//    than 2^8 (the rescale is exact; weights up to 256 are fine in bf16/fp32),
+//    and that rare rescale runs outside the hot chunk loop;
+//  * items are taken from a work counter in order of decreasing sequence
+//    length (the plan kernel sorts up to 512 prefill sequences), so the
+//    longest items start first.
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+#include "tiles.h"
+
+namespace pkv {
+
+namespace {
+constexpr int kPfWaves = 8;                        // 2 per SIMD
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfTiles = 2;                        // 16-column tiles per wave
+constexpr int kPfWaveCols = 16 * kPfTiles;         // 64
+constexpr int kPfCols = kPfWaveCols * kPfWaves;    // 256 columns per item
+constexpr int kPlanHeader = 16;                    // ints: [0] items, [1] prefill seqs, [2] counter
+constexpr int kSortMax = 512;
+constexpr float kRescaleSlack = 8.f;               // log2 units
+}  // namespace
+
+// plan (ints): header, then the processing order of the prefill sequences
+// [B], their item prefix sums [B + 1], and scan scratch [B + 1].
+size_t prefill_plan_bytes(int num_seqs) {
+  return ((size_t)(kPlanHeader + 3 * (size_t)num_seqs + 2) * 4 + 255) / 256 * 256;
+}
+
+// Exclusive scan of f(i), i in [0, n), writing out(i, prefix) for i in [0, n]
+// (out(n, total)); LDS use is independent of n.  Ends with a barrier.
+template <typename F, typename O>
+__device__ int block_scan_to(int n, F f, O out) {
+  __shared__ int wave_tot[256 / kWave];
+  const int tid = threadIdx.x, wid = tid / kWave;
+  int carry = 0;
+  for (int base = 0; base < n; base += 256) {
+    const int i = base + tid;
+    const int v = i < n ? f(i) : 0;
+    int x = wave_inclusive_scan(v);
+    if (lane_id() == kWave - 1) wave_tot[wid] = x;
+    __syncthreads();
+    int off = carry;
+    for (int w = 0; w < wid; ++w) off += wave_tot[w];
+    if (i < n) out(i, x + off - v);
+    int tot = 0;
+    for (int w = 0; w < 256 / kWave; ++w) tot += wave_tot[w];
+    carry += tot;
+    __syncthreads();
+  }
+  if (tid == 0) out(n, carry);
+  __syncthreads();
+  return carry;
+}
+
+__global__ void __launch_bounds__(256)
+prefill_plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int B, int max_tok,
+                    int Hkv, int G, int* __restrict__ plan) {
+  __shared__ int s_len[kSortMax];
+  __shared__ int s_seq[kSortMax];
+  int* order = plan + kPlanHeader;
+  int* cum = order + B;
+  int* pre = cum + B + 1;                              // scratch: prefix of "is prefill"
+  auto is_prefill = [&](int s) { return qsl[s + 1] - qsl[s] > 1 ? 1 : 0; };
+  const int P = block_scan_to(B, is_prefill, [&](int i, int v) { pre[i] = v; });
+  auto len = [&](int s) {
+    const int L = seq_lens[s];
+    return L < 0 ? 0 : (L > max_tok ? max_tok : L);
+  };
+  if (P <= kSortMax) {
+    for (int s = threadIdx.x; s < B; s += 256)
+      if (pre[s + 1] != pre[s]) {
+        s_seq[pre[s]] = s;
+        s_len[pre[s]] = len(s);
+      }
+    __syncthreads();
+    // rank: longer first, ties by sequence index
+    for (int i = threadIdx.x; i < P; i += 256) {
+      int rank = 0;
+      for (int j = 0; j < P; ++j)
+        rank += (s_len[j] > s_len[i]) || (s_len[j] == s_len[i] && j < i);
+      order[rank] = s_seq[i];
+    }
+  } else {
+    for (int s = threadIdx.x; s < B; s += 256)
+      if (pre[s + 1] != pre[s]) order[pre[s]] = s;
+  }
+  __syncthreads();
+  auto items = [&](int r) {
+    const int s = order[r];
+    const int q = qsl[s + 1] - qsl[s];
+    return Hkv * ((q * G + kPfCols - 1) / kPfCols);
+  };
+  const int total = block_scan_to(P, items, [&](int i, int v) { cum[i] = v; });
+  if (threadIdx.x == 0) {
+    plan[0] = total;
+    plan[1] = P;
+    plan[2] = 0;                                       // work counter
+  }
+}
+
+template <int BS>
+__global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
+prefill_lds_kernel(const PrefillArgs a) {
+  typedef TileBf16<128, BS> Tile;
+  constexpr int D = 128, NDT = 8, RB = 256;            // row bytes of one KV head
+  __shared__ __attribute__((aligned(16))) uint8_t kvbuf[2][2][32 * RB];   // [buffer][K|V][32 rows]
+  __shared__ int s_item;
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, col = l & 15, c = l >> 4;
+  const int B = a.num_seqs, G = a.group, Hkv = a.num_kv_heads, Hq = a.num_q_heads;
+  const int max_tok = a.max_blocks * BS;
+  const int* plan = a.plan;
+  const int total = plan[0], P = plan[1];
+  const int* order = plan + kPlanHeader;
+  const int* cum = order + B;
+  int* counter = a.plan + 2;
+  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.key_cache);
+  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.value_cache);
+  const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.query);
+  const int ld_row = tid >> 4, ld_chunk = tid & 15;    // loader: 16 lanes per 256 B row (32 rows)
+
+  while (true) {
+    __syncthreads();                                   // everyone has read the previous item
+    if (tid == 0) s_item = atomicAdd(counter, 1);
+    __syncthreads();
+    const int item = s_item;
+    if (item >= total) break;
+    int lo = 0, hi = P;                                // last r with cum[r] <= item
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cum[mid] <= item) lo = mid; else hi = mid;
+    }
+    const int s = uniform(order[lo]);
+    const int local = uniform(item - cum[lo]);
+    const int qrow0 = uniform(a.qsl[s]);
+    const int q_s = uniform(a.qsl[s + 1]) - qrow0;
+    const int per_head = (q_s * G + kPfCols - 1) / kPfCols;
+    const int h = local / per_head;
+    const int cb = per_head - 1 - (local - h * per_head);   // most rows first
+    int L = uniform(a.seq_lens[s]);
+    L = L < 0 ? 0 : (L > max_tok ? max_tok : L);
+    const int ctx = L - q_s;
+    const int f0 = cb * kPfCols, f1 = min(f0 + kPfCols, q_s * G);
+    const int p_max = ctx + (f1 - 1) / G;              // last key any column of the item sees
+    if (p_max < 0) continue;                           // seq_len < rows: nothing is defined
+    const int f0w = f0 + wave * kPfWaveCols, f1w = min(f0w + kPfWaveCols, f1);
+    const bool has = f0w < f1w;
+    const int p_min_w = ctx + f0w / G;
+    const int p_max_w = has ? ctx + (f1w - 1) / G : -1;
+
+    typename Tile::Q q[kPfTiles];
+    int pos[kPfTiles];
+#pragma unroll
+    for (int t = 0; t < kPfTiles; ++t) {
+      const int f = f0w + 16 * t + col;
+      const int row = f / G, head = f - row * G;
+      pos[t] = ctx + row;
+      Tile::load_q_col(q[t], qbase + ((int64_t)(qrow0 + row) * Hq + h * G + head) * D, f < f1w);
+    }
+
+    BlockWindow win;
+    win.row = a.block_tables + (int64_t)s * a.max_blocks;
+    win.nblk = (L + BS - 1) / BS;
+    win.max_id = a.num_blocks - 1;
+    win.fill(0);
+
+    // Loader: piece k of this thread is row ld_row (0..31) of the K (k = 0) or
+    // V (k = 1) chunk, bytes 16 * ld_chunk; rows past p_max load zeros.
+    u32x4 R[2];
+    auto load_chunk = [&](int ch) {
+      const int tok = ch * 32 + ld_row;
+      const int lb0 = (ch * 32) / BS;                          // uniform
+      const int blk = BS == 16 ? (ld_row < 16 ? win.get(lb0) : win.get(lb0 + 1)) : win.get(lb0);
+      const int off = tok - (BS == 16 ? (lb0 + (ld_row >> 4)) : lb0) * BS;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint16_t* base = (k == 0 ? kc : vc) + ((int64_t)blk * BS + off) * Hkv * D + h * D + 8 * ld_chunk;
+        R[k] = tok <= p_max ? ld16(base) : u32x4{0, 0, 0, 0};
+      }
+    };
+    auto store_chunk = [&](int b) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        *reinterpret_cast<u32x4*>(&kvbuf[b][k][ld_row * RB + ((ld_chunk ^ (ld_row & 15)) << 4)]) = R[k];
+    };
+
+    float mref[kPfTiles], lsum[kPfTiles];
+    f32x4 o[kPfTiles][NDT];
+#pragma unroll
+    for (int t = 0; t < kPfTiles; ++t) {
+      mref[t] = -INFINITY;
+      lsum[t] = 0.f;
+#pragma unroll
+      for (int d = 0; d < NDT; ++d) o[t][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Phase A of a chunk: scores of all tiles from the shared K tile, masked
+    // on diagonal chunks, and each column's scaled maximum.
+    f32x4 sc[kPfTiles][2];
+    float cmx[kPfTiles];
+    auto scores = [&](int b, int ch, auto diag_tag) {
+      constexpr bool DIAG = decltype(diag_tag)::value;
+      const uint8_t* Kt = kvbuf[b][0];
+      u32x4 kop[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int row = 16 * u + col;
+          kop[u][kk] = *reinterpret_cast<const u32x4*>(Kt + row * RB + (((4 * kk + c) ^ (row & 15)) << 4));
+        }
+#pragma unroll
+      for (int t = 0; t < kPfTiles; ++t) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          sc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            sc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[u][kk]),
+                                                               __builtin_bit_cast(bf16x8, q[t].q[kk]), sc[t][u], 0, 0, 0);
+        }
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if constexpr (DIAG) sc[t][u][r] = (ch * 32 + 16 * u + 4 * c + r <= pos[t]) ? sc[t][u][r] : -INFINITY;
+            cmax = fmaxf(cmax, sc[t][u][r]);
+          }
+        cmx[t] = wave_max_across_rows(cmax) * a.scale_log2;
+      }
+    };
+    // Phase B: weights against the current reference maxima, then O^T += V^T P^T.
+    auto accumulate = [&](int b) {
+      const uint8_t* Vt = kvbuf[b][1];
+      bf16x8 pb[kPfTiles];
+#pragma unroll
+      for (int t = 0; t < kPfTiles; ++t) {
+        float ps = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = fast_exp2(fmaf(sc[t][u][r], a.scale_log2, -mref[t]));
+            ps += p;
+            pb[t][4 * u + r] = (__bf16)p;
+          }
+        lsum[t] += ps;
+      }
+      u32x4 vr[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * u + 4 * c + r;
+          vr[u][r] = *reinterpret_cast<const u32x4*>(Vt + row * RB + ((col ^ (row & 15)) << 4));
+        }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        u32x4 av;
+        av[0] = Tile::pick(vr[0][0], vr[0][1], dt);
+        av[1] = Tile::pick(vr[0][2], vr[0][3], dt);
+        av[2] = Tile::pick(vr[1][0], vr[1][1], dt);
+        av[3] = Tile::pick(vr[1][2], vr[1][3], dt);
+#pragma unroll
+        for (int t = 0; t < kPfTiles; ++t)
+          o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb[t], o[t][dt], 0, 0, 0);
+      }
+    };
+
+    const int nch = (p_max + 32) / 32;
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+    // The hot loop touches O only through MFMAs.  When a column's maximum
+    // outgrows its reference by more than the slack (always on the first
+    // chunk), the wave leaves the loop before the chunk's PV and barrier,
+    // rescales in the outer loop, and re-enters at the same chunk.
+    int ch = 0;
+    while (true) {
+      for (; ch < nch; ++ch) {
+        if (ch + 1 < nch) load_chunk(ch + 1);
+        if (has && ch * 32 <= p_max_w) {
+          if (ch * 32 + 31 > p_min_w) scores(ch & 1, ch, std::true_type{});
+          else scores(ch & 1, ch, std::false_type{});
+          bool need = false;
+#pragma unroll
+          for (int t = 0; t < kPfTiles; ++t) need |= cmx[t] > mref[t] + kRescaleSlack;
+          if (__any(need)) break;
+          accumulate(ch & 1);
+        }
+        if (ch + 1 < nch) store_chunk((ch + 1) & 1);
+        __syncthreads();
+      }
+      if (ch >= nch) break;
+#pragma unroll
+      for (int t = 0; t < kPfTiles; ++t) {
+        const bool need = cmx[t] > mref[t] + kRescaleSlack;
+        const float alpha = need ? fast_exp2(mref[t] - cmx[t]) : 1.f;   // 0 on the first chunk
+        mref[t] = need ? cmx[t] : mref[t];
+        lsum[t] *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDT; ++d) o[t][d] *= alpha;
+      }
+    }
+
+#pragma unroll
+    for (int t = 0; t < kPfTiles; ++t) {
+      const float tot = wave_sum_across_rows(lsum[t]);
+      const int f = f0w + 16 * t + col;
+      if (f >= f1w) continue;
+      const int row = f / G, head = f - row * G;
+      const float inv = 1.f / tot;
+      float* dst = a.out + ((int64_t)(qrow0 + row) * Hq + h * G + head) * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int g = 0; g < NDT / 4; ++g)
+          st16f(dst + Tile::out_dim(4 * g, c, r),
+                f32x4{o[t][4 * g][r] * inv, o[t][4 * g + 1][r] * inv, o[t][4 * g + 2][r] * inv,
+                      o[t][4 * g + 3][r] * inv});
+    }
+  }
+}
+
+hipError_t launch_prefill_lds(const PrefillArgs& a, int block_size, int cus, hipStream_t stream) {
+  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(256), 0, stream, a.qsl, a.seq_lens, a.num_seqs,
+                     a.max_blocks * block_size, a.num_kv_heads, a.group, a.plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int grid = cus > 0 ? cus : 256;
+  if (block_size == 16)
+    hipLaunchKernelGGL(prefill_lds_kernel<16>, dim3(grid), dim3(kPfThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_lds_kernel<32>, dim3(grid), dim3(kPfThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -231,7 +231,9 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool bf16, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool bf16, int cus,
+                          hipStream_t stream) {
+  if (bf16 && head_dim == 128) return launch_prefill_lds(a, block_size, cus, stream);
 #define PKV_CASE(T, B, D, BS) \
   if (head_dim == D && block_size == BS) return launch_prefill_t<T<D, BS>, PrefillTiles<B, D>::value>(a, stream);
   if (bf16) {
