@@ -4,8 +4,9 @@
 
 A step is one decode iteration of the 128-sequence GQA workload (64 query /
 8 KV heads, head_dim 128, bf16 KV, 16-token blocks, lognormal lengths with
-median 1500 clipped to [16, 8192]): slot mapping of the step's new tokens ->
-reshape_and_cache -> paged decode attention (split kernel + merge kernel).
+median 1500 clipped to [16, 8192]): slot mapping and cache write of the
+step's new tokens (pkv_write_new_tokens, one kernel) -> paged decode
+attention (split kernel + merge kernel).
 Inputs are resident in HBM before timing starts.  Prints one JSON line.
 --config N runs another seeded workload the same way (1-4 decode; 5 is the
 mixed chunked-prefill + decode step, timed through the varlen call, whose
@@ -210,8 +211,8 @@ def main() -> int:
     torch.cuda.synchronize()
 
     def step():
-        ops.compute_slot_mapping(bt, pos, qsl, sp.block_size, out=slots)
-        ops.reshape_and_cache(key, value, kc, vc, slots)
+        # slot mapping + cache write of the step's new tokens (one fused kernel)
+        ops.write_new_tokens(bt, pos, qsl, sp.block_size, key, value, kc, vc, slots)
         if varlen:
             ops.paged_attention_varlen(q, kc, vc, bt, sl, qsl, wl.scale, wl.max_query_len, wl.max_seq_len,
                                        out=out, workspace=ws)
@@ -289,7 +290,8 @@ def main() -> int:
         "config": {"workload": sp.name, "num_seqs": wl.num_seqs, "num_q_heads": sp.num_q_heads,
                    "num_kv_heads": sp.num_kv_heads, "head_dim": sp.head_dim, "block_size": sp.block_size,
                    "sum_seq_len": int(wl.seq_lens.sum()), "max_seq_len": wl.max_seq_len, "seed": wl.seed,
-                   "step": "slot_mapping + reshape_and_cache + paged_attention_%s" % ("varlen" if varlen else "decode")},
+                   "step": "write_new_tokens (slot mapping + reshape_and_cache) + paged_attention_%s"
+                           % ("varlen" if varlen else "decode")},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "seq_tokens_per_s": round(wl.num_tokens / (ms_step * 1e-3), 1),
         "kv_tokens_per_s": round(float(wl.seq_lens.sum()) / (ms_step * 1e-3), 1),

@@ -110,6 +110,20 @@ int pkv_reshape_and_cache(const void* key, const void* value, void* key_cache, v
                           void* stream);
 
 /*
+ * pkv_compute_slot_mapping followed by pkv_reshape_and_cache, fused into one
+ * kernel launch (same results, bit for bit): each new token's slot is computed
+ * as pkv_compute_slot_mapping defines it and its K and V rows are copied
+ * there.  Arguments are those of the two calls; slot_mapping may be NULL
+ * (slots are then not stored).  Tokens whose slot is -1 or beyond the pool are
+ * skipped.
+ */
+int pkv_write_new_tokens(const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                         const int32_t* positions, const int32_t* query_start_loc, int32_t num_tokens,
+                         int32_t block_size, const void* key, const void* value, void* key_cache,
+                         void* value_cache, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                         pkv_dtype dtype, int64_t* slot_mapping, void* stream);
+
+/*
  * Bytes of device workspace pkv_paged_attention_decode needs for this shape
  * on the CURRENT device (the split of the work depends on its compute-unit
  * count).  Returns 0 for shapes the library does not support.

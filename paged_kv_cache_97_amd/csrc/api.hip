@@ -155,6 +155,31 @@ int pkv_reshape_and_cache(const void* key, const void* value, void* key_cache, v
   return e == hipSuccess ? ok() : hip_fail(e, "reshape_and_cache launch");
 }
 
+int pkv_write_new_tokens(const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                         const int32_t* positions, const int32_t* query_start_loc, int32_t num_tokens,
+                         int32_t block_size, const void* key, const void* value, void* key_cache,
+                         void* value_cache, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                         pkv_dtype dtype, int64_t* slot_mapping, void* stream) {
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_blocks < 0 || block_size <= 0)
+    return fail(PKV_EINVAL, "bad size (tokens %d, seqs %d, max_blocks %d, kv_heads %d, head_dim %d, blocks %lld, "
+                "block_size %d)", num_tokens, num_seqs, max_blocks_per_seq, num_kv_heads, head_dim,
+                (long long)num_blocks, block_size);
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "dtype %d", (int)dtype);
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * elem_bytes(dtype);
+  if (row_bytes % 16) return fail(PKV_EUNSUPPORTED, "token row of %lld bytes is not a multiple of 16", (long long)row_bytes);
+  if (num_tokens == 0) return ok();
+  if (!positions || !query_start_loc || !key || !value || !key_cache || !value_cache ||
+      (num_seqs > 0 && max_blocks_per_seq > 0 && !block_tables))
+    return fail(PKV_EINVAL, "null pointer");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PKV_EINVAL, "key/value/cache pointers must be 16-byte aligned");
+  hipError_t e = pkv::launch_write_tokens(block_tables, num_seqs, max_blocks_per_seq, positions, query_start_loc,
+                                          num_tokens, block_size, key, value, key_cache, value_cache, (int)row_bytes,
+                                          num_blocks * block_size, slot_mapping, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "write_new_tokens launch");
+}
+
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, pkv_dtype dtype) {
   if (num_seqs < 0 || num_seqs > kMaxSeqs) return 0;

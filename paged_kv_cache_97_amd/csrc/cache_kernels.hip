@@ -65,6 +65,73 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
   }
 }
 
+// Slot mapping and cache write of a step's new tokens in one launch: each
+// workgroup takes kTokensPerWg tokens, a few lanes compute their slots (owner
+// search over query_start_loc staged in LDS), then all lanes copy the rows.
+constexpr int kTokensPerWg = 8;
+constexpr int kQslLds = 1024;
+
+__global__ void __launch_bounds__(256)
+write_tokens_kernel(const int32_t* __restrict__ block_tables, int num_seqs, int max_blocks,
+                    const int32_t* __restrict__ positions, const int32_t* __restrict__ qsl, int num_tokens,
+                    int block_size, const u32x4* __restrict__ key, const u32x4* __restrict__ value,
+                    u32x4* __restrict__ key_cache, u32x4* __restrict__ value_cache, int row_vecs,
+                    int64_t num_slots, int64_t* __restrict__ slots_out) {
+  __shared__ int qs[kQslLds];
+  __shared__ int64_t s_slot[kTokensPerWg];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kTokensPerWg;
+  const bool staged = num_seqs + 1 <= kQslLds;
+  if (staged)
+    for (int i = tid; i <= num_seqs; i += 256) qs[i] = qsl[i];
+  __syncthreads();
+  if (tid < kTokensPerWg) {
+    const int t = t0 + tid;
+    int64_t slot = -1;
+    if (t < num_tokens) {
+      const int32_t* q = staged ? qs : qsl;
+      int lo = 0, hi = num_seqs;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (q[mid] <= t) lo = mid; else hi = mid;
+      }
+      const int p = positions[t];
+      if (num_seqs > 0 && t < q[lo + 1] && p >= 0) {
+        const int lb = p / block_size;
+        if (lb < max_blocks) {
+          const int phys = block_tables[(int64_t)lo * max_blocks + lb];
+          if (phys >= 0) slot = (int64_t)phys * block_size + (p - lb * block_size);
+        }
+      }
+      if (slots_out) slots_out[t] = slot;
+    }
+    s_slot[tid] = slot;
+  }
+  __syncthreads();
+  const int n = min(kTokensPerWg, num_tokens - t0) * row_vecs;
+  for (int i = tid; i < n; i += 256) {
+    const int tl = i / row_vecs, cvec = i - tl * row_vecs;
+    const int64_t slot = s_slot[tl];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t src = (int64_t)(t0 + tl) * row_vecs + cvec;
+    const u32x4 k = key[src];
+    const u32x4 v = value[src];
+    key_cache[slot * row_vecs + cvec] = k;
+    value_cache[slot * row_vecs + cvec] = v;
+  }
+}
+
+hipError_t launch_write_tokens(const int32_t* bt, int num_seqs, int max_blocks, const int32_t* pos,
+                               const int32_t* qsl, int num_tokens, int block_size, const void* key,
+                               const void* value, void* kc, void* vc, int row_bytes, int64_t num_slots,
+                               int64_t* slots, hipStream_t stream) {
+  const int blocks = (num_tokens + kTokensPerWg - 1) / kTokensPerWg;
+  hipLaunchKernelGGL(write_tokens_kernel, dim3(blocks), dim3(256), 0, stream, bt, num_seqs, max_blocks, pos, qsl,
+                     num_tokens, block_size, (const u32x4*)key, (const u32x4*)value, (u32x4*)kc, (u32x4*)vc,
+                     row_bytes / 16, num_slots, slots);
+  return hipGetLastError();
+}
+
 hipError_t launch_slot_mapping(const int32_t* bt, int num_seqs, int max_blocks, const int32_t* pos,
                                const int32_t* qsl, int num_tokens, int block_size, int64_t* slots,
                                hipStream_t stream) {

@@ -50,6 +50,11 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc
                                     const int64_t* slots, int num_tokens, int row_bytes,
                                     int64_t num_slots, hipStream_t stream);
 
+hipError_t launch_write_tokens(const int32_t* bt, int num_seqs, int max_blocks, const int32_t* pos,
+                               const int32_t* qsl, int num_tokens, int block_size, const void* key,
+                               const void* value, void* kc, void* vc, int row_bytes, int64_t num_slots,
+                               int64_t* slots, hipStream_t stream);
+
 }  // namespace pkv
 
 namespace pkv {

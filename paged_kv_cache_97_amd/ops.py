@@ -26,6 +26,8 @@ _SIGNATURES = {
     "pkv_compute_slot_mapping": (_c_i32, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp]),
     "pkv_reshape_and_cache": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i64,
                                        _c_i32, _c_i32, _c_vp]),
+    "pkv_write_new_tokens": (_c_i32, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
+                                      _c_vp, _c_i32, _c_i32, _c_i64, _c_i32, _c_vp, _c_vp]),
     "pkv_decode_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pkv_paged_attention_decode": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32, _c_i32,
                                             _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_f32, _c_i32, _c_vp,
@@ -127,6 +129,30 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.T
                                        _dev(key_cache, "key_cache", ndim=4), _dev(value_cache, "value_cache", ndim=4),
                                        _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, Hkv, D, NB, bs,
                                        _kv_dtype(key), _stream(key)), "reshape_and_cache")
+
+
+def write_new_tokens(block_tables: torch.Tensor, positions: torch.Tensor, query_start_loc: torch.Tensor,
+                     block_size: int, key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                     value_cache: torch.Tensor, slot_mapping: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """compute_slot_mapping + reshape_and_cache in one kernel; returns the
+    slots if ``slot_mapping`` is given (written in place)."""
+    B, M = block_tables.shape
+    T, Hkv, D = key.shape
+    NB, bs = key_cache.shape[0], key_cache.shape[1]
+    if value.shape != key.shape or value_cache.shape != key_cache.shape or key_cache.shape[2:] != (Hkv, D):
+        raise ValueError("key/value/cache shapes disagree")
+    if key.dtype != key_cache.dtype or value.dtype != key.dtype or value_cache.dtype != key.dtype:
+        raise ValueError("key/value/caches must share one dtype")
+    if positions.shape[0] != T or query_start_loc.shape[0] != B + 1 or bs != block_size:
+        raise ValueError("positions/query_start_loc/block_size do not match")
+    sp = _dev(slot_mapping, "slot_mapping", torch.int64, 1) if slot_mapping is not None else None
+    _check(lib().pkv_write_new_tokens(_dev(block_tables, "block_tables", torch.int32, 2), B, M,
+                                      _dev(positions, "positions", torch.int32, 1),
+                                      _dev(query_start_loc, "query_start_loc", torch.int32, 1), T, int(block_size),
+                                      _dev(key, "key", ndim=3), _dev(value, "value", ndim=3),
+                                      _dev(key_cache, "key_cache", ndim=4), _dev(value_cache, "value_cache", ndim=4),
+                                      Hkv, D, NB, _kv_dtype(key), sp, _stream(key)), "write_new_tokens")
+    return slot_mapping
 
 
 def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,

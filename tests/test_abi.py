@@ -66,6 +66,18 @@ def test_empty_work_enqueues_nothing():
     assert lib.pkv_reshape_and_cache(None, None, None, None, None, 3, 1, 4, 0, 16, 1, None) == 2
 
 
+def test_fused_write_validation():
+    lib = ops.lib()
+    args = [None, 2, 4, None, None, 0, 16, None, None, None, None, 8, 128, 10, 1, None, None]
+    assert lib.pkv_write_new_tokens(*args) == 0                   # no tokens: nothing enqueued
+    args[5] = 3
+    assert lib.pkv_write_new_tokens(*args) == 1                   # null pointers
+    bad = list(args); bad[11] = 1; bad[12] = 4
+    assert lib.pkv_write_new_tokens(*bad) == 2                    # 8-byte rows
+    bad = list(args); bad[14] = 9
+    assert lib.pkv_write_new_tokens(*bad) == 2                    # dtype
+
+
 def test_workspace_size_rules():
     lib = ops.lib()
     assert lib.pkv_decode_workspace_size(128, 64, 8, 128, 16, 1) > 0
