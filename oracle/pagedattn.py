@@ -17,6 +17,10 @@ What it computes, and where the pages state it:
   * attention -- gaoleia §1.6: gather K and V of the sequence's blocks in
     logical order, keep the first seq_len tokens, then softmax(q K^T / sqrt(d))
     V.  Paging only moves where K/V live, so this is exact dense attention.
+  * copy_blocks / swap_blocks -- lakecityint.com/news/209622 §3.2 (copy-on-
+    write: a new physical block receives a copy of the shared block before
+    one sharer writes) and §2.1, 5688vip.com "vLLM核心机制" §3.3 (preemption
+    swaps a sequence's blocks out to CPU memory and back in later).
   * varlen rows -- gaoleia §2.4 (one iteration mixes decode rows and prefill
     rows) and §2.5 (a long prompt is cut into 512-token chunks interleaved
     with decodes); fanquanpp.github.io "vLLM服务内部" 分块预填充.  A chunk of q
@@ -39,7 +43,7 @@ import numpy as np
 __all__ = [
     "to_f64", "slot_mapping", "reshape_and_cache", "gather_tokens",
     "decode_attention", "varlen_attention", "attention_rows",
-    "partial_attention", "combine_partials",
+    "partial_attention", "combine_partials", "copy_blocks", "swap_blocks",
 ]
 
 
@@ -208,3 +212,37 @@ def combine_partials(parts):
     Z = sum(np.exp(m - M) * z for m, z, _ in parts)
     o = sum(np.exp(m - M) * ok for m, _, ok in parts)
     return o / Z
+
+
+def _check_mapping(mapping, n_src, n_dst, same_pool):
+    pairs = [(int(a), int(b)) for a, b in np.asarray(mapping).reshape(-1, 2)]
+    dsts = [b for _, b in pairs]
+    assert len(dsts) == len(set(dsts)), "two copies into one block"
+    assert all(0 <= a < n_src and 0 <= b < n_dst for a, b in pairs), "block id outside the pool"
+    if same_pool:
+        assert not set(dsts) & {a for a, _ in pairs}, "a destination is also a source"
+    return pairs
+
+
+def copy_blocks(key_cache, value_cache, mapping):
+    """Copy-on-write block copies inside the pools (lakecityint §3.2): for
+    each (src, dst) pair block dst becomes a bit copy of block src, K and V.
+    Destinations are distinct and are not sources of the same call."""
+    pairs = _check_mapping(mapping, key_cache.shape[0], key_cache.shape[0], True)
+    kc = np.array(key_cache, copy=True)
+    vc = np.array(value_cache, copy=True)
+    for src, dst in pairs:
+        kc[dst] = key_cache[src]
+        vc[dst] = value_cache[src]
+    return kc, vc
+
+
+def swap_blocks(src_pool, dst_pool, mapping):
+    """Swap-out / swap-in of whole blocks between two pools (GPU <-> CPU;
+    5688vip §3.3, lakecityint §2.1): block dst of dst_pool becomes a bit copy
+    of block src of src_pool."""
+    pairs = _check_mapping(mapping, src_pool.shape[0], dst_pool.shape[0], False)
+    out = np.array(dst_pool, copy=True)
+    for src, dst in pairs:
+        out[dst] = src_pool[src]
+    return out

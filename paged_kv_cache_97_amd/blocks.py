@@ -18,11 +18,16 @@ Sources (the pages describe the structures, they ship no allocator):
     every table tracks its true token count instead (the num_tokens field of
     §1.3 on the gaoleia page).
   * lakecityint.com/news/209622 §4.2 (BlockManager.allocate_block pops a free
-    block; exhaustion is the preemption trigger).
+    block; exhaustion is the preemption trigger), §3.2 (copy-on-write: a
+    sharer about to write gets a new block, the shared block's content is
+    copied into it, its table is remapped and the old block loses one
+    reference) and §2.1 (preempted sequences wait in a swapped queue with
+    their blocks in CPU memory); 5688vip.com §3.3 (preemption swaps out to
+    CPU or releases the blocks and recomputes later).
 """
 from __future__ import annotations
 
-from typing import Iterable, List, Optional, Sequence
+from typing import Iterable, List, Optional, Sequence, Tuple
 
 
 class BlockPool:
@@ -122,6 +127,40 @@ class SeqBlocks:
             self.append_block(b)
         self.num_tokens = n_blocks * self.block_size
 
+    def fork(self, pool: BlockPool) -> "SeqBlocks":
+        """A new table sharing every block of this one, including a partly
+        filled last block (parallel sampling from one prompt)."""
+        child = SeqBlocks(self.block_size)
+        for b in self.mapping:
+            pool.incref(b)
+            child.append_block(b)
+        child.num_tokens = self.num_tokens
+        return child
+
+    def prepare_write(self, logical_idx: int, pool: BlockPool) -> Optional[Tuple[int, int]]:
+        """Copy-on-write before writing into logical block ``logical_idx``: a
+        block other tables still reference is replaced by a fresh block that
+        must receive a copy of it.  Returns (old, new) for the device copy, or
+        None when the block is already private."""
+        old = self.mapping[logical_idx]
+        if pool.ref_count(old) <= 1:
+            return None
+        new = pool.alloc()
+        self.mapping[logical_idx] = new
+        pool.free(old)                       # drop this table's reference
+        return old, new
+
+    def prepare_append(self, n: int, pool: BlockPool) -> List[Tuple[int, int]]:
+        """Room for ``n`` more tokens, copying a shared partly filled last
+        block first; returns the (old, new) copies the device must make."""
+        copies = []
+        if n > 0 and self.mapping and self.num_tokens % self.block_size:
+            cw = self.prepare_write(len(self.mapping) - 1, pool)
+            if cw:
+                copies.append(cw)
+        self.append_tokens(n, pool)
+        return copies
+
     def release(self, pool: BlockPool) -> None:
         for b in self.mapping:
             pool.free(b)
@@ -139,3 +178,35 @@ def tables_to_rows(tables: Sequence[SeqBlocks], width: Optional[int] = None) -> 
     w = max((len(t.mapping) for t in tables), default=0) if width is None else width
     w = max(w, 1)
     return [t.row(w) for t in tables]
+
+
+def swap_out(table: SeqBlocks, gpu_pool: BlockPool, cpu_pool: BlockPool) -> List[Tuple[int, int]]:
+    """Move a table's blocks to CPU blocks: returns (gpu, cpu) copies to make
+    before the GPU blocks are reused; the table then holds CPU ids.  A block
+    other tables share stays on the GPU for them (only a reference is
+    dropped) and this table gets its own CPU copy.  Raises MemoryError, and
+    changes nothing, when the CPU pool lacks room."""
+    if cpu_pool.num_free() < len(table.mapping):
+        raise MemoryError("CPU pool has %d free blocks, %d needed" % (cpu_pool.num_free(), len(table.mapping)))
+    pairs = []
+    for i, b in enumerate(table.mapping):
+        c = cpu_pool.alloc()
+        pairs.append((b, c))
+        gpu_pool.free(b)
+        table.mapping[i] = c
+    return pairs
+
+
+def swap_in(table: SeqBlocks, cpu_pool: BlockPool, gpu_pool: BlockPool) -> List[Tuple[int, int]]:
+    """Bring a swapped table back: returns (cpu, gpu) copies; the CPU blocks
+    are free again once the copies are done.  Raises MemoryError, and changes
+    nothing, when the GPU pool lacks room."""
+    if gpu_pool.num_free() < len(table.mapping):
+        raise MemoryError("GPU pool has %d free blocks, %d needed" % (gpu_pool.num_free(), len(table.mapping)))
+    pairs = []
+    for i, c in enumerate(table.mapping):
+        g = gpu_pool.alloc()
+        pairs.append((c, g))
+        cpu_pool.free(c)
+        table.mapping[i] = g
+    return pairs
