@@ -10,7 +10,8 @@ attention (split kernel + merge kernel).
 Inputs are resident in HBM before timing starts.  Prints one JSON line.
 --config N runs another seeded workload the same way (1-4 decode; 5 is the
 mixed chunked-prefill + decode step, timed through the varlen call, whose
-dominant kernel is the MFMA-bound prefill kernel).
+dominant kernel is the MFMA-bound prefill kernel).  --blocks times the
+copy-on-write block copy and the swap to and from pinned host memory.
 
 value = KV bytes read per step / step time (GB/s, 1 GB = 1e9 B), where KV
 bytes = sum(seq_len) * 2 (K and V) * num_kv_heads * head_dim * 2 B -- each
@@ -156,6 +157,63 @@ def _cpu_baseline(wl, budget_s: float = 12.0):
             "seq_tokens_per_s": round(rows / dt, 3)}
 
 
+def bench_blocks(args) -> int:
+    """Block copies at the decode workload's block shape (16 tokens x 8 KV
+    heads x 128 dims bf16 = 32 KiB per pool): copy-on-write copies inside a
+    GPU pool and a swap-out / swap-in of a batch of blocks through pinned host
+    memory.  One JSON line; bytes count reads plus writes of K and V."""
+    import torch
+    from paged_kv_cache_97_amd import ops
+    dev = torch.device("cuda:0")
+    bs, Hkv, D = 16, 8, 128
+    NB, pairs, NC = 65536, 4096, 8192
+    rng = np.random.default_rng(0)
+    kc = torch.randn(NB, bs, Hkv, D, device=dev).to(torch.bfloat16)
+    vc = torch.randn(NB, bs, Hkv, D, device=dev).to(torch.bfloat16)
+    ids = rng.permutation(NB)[:2 * pairs]
+    cow = torch.from_numpy(np.stack([ids[:pairs], ids[pairs:]], 1).astype(np.int64)).to(dev)
+    hk = torch.empty(NC, bs, Hkv, D, dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk).pin_memory()
+    out_map = torch.from_numpy(np.stack([ids[:pairs], rng.permutation(NC)[:pairs]], 1).astype(np.int64)).to(dev)
+    in_map = torch.from_numpy(np.stack([out_map[:, 1].cpu().numpy(), ids[pairs:]], 1).astype(np.int64)).to(dev)
+    blk = bs * Hkv * D * 2
+    moved = 2 * pairs * blk                         # K and V blocks per call (each read once, written once)
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_copy = timed(lambda: ops.copy_blocks(kc, vc, cow), args.steps)
+    ms_out = timed(lambda: ops.swap_blocks(kc, vc, hk, hv, out_map), max(2, args.steps // 10))
+    ms_in = timed(lambda: ops.swap_blocks(hk, hv, kc, vc, in_map), max(2, args.steps // 10))
+    print("bench: copy %.4f ms, swap-out %.4f ms, swap-in %.4f ms (%d pairs of 2 x %d B)" % (
+        ms_copy, ms_out, ms_in, pairs, blk), file=sys.stderr, flush=True)
+    copy_gbs = 2 * moved / (ms_copy * 1e-3) / 1e9
+    rec = {
+        "metric": "block copy GB/s (HBM read + write) and swap GB/s (PCIe, one direction)",
+        "value": round(copy_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_copy, 5), "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "cow-copy-4096-blocks-bs16-h8-d128-bf16", "pairs": pairs, "block_bytes": blk,
+                   "pool_blocks": NB, "host_blocks": NC},
+        "roofline": {"bound": "hbm", "kernel": "block_copy_kernel", "achieved": round(copy_gbs, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(copy_gbs / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": 2 * moved},
+        "swap_out_gbs": round(moved / (ms_out * 1e-3) / 1e9, 2),
+        "swap_in_gbs": round(moved / (ms_in * 1e-3) / 1e9, 2),
+        "swap_out_ms": round(ms_out, 4), "swap_in_ms": round(ms_in, 4),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +226,8 @@ def main() -> int:
     ap.add_argument("--summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of --kernels-only into %s" % os.path.relpath(TRAFFIC_FILE, ROOT))
     ap.add_argument("--command", default="", help="command line recorded with --summarize")
+    ap.add_argument("--blocks", action="store_true",
+                    help="time the copy-on-write block copy and the GPU <-> pinned host swap instead")
     args = ap.parse_args()
     if args.summarize:
         from paged_kv_cache_97_amd import workloads as W
@@ -188,6 +248,8 @@ def main() -> int:
     from paged_kv_cache_97_amd import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.blocks:
+        return bench_blocks(args)
     dev = torch.device("cuda:0")
     ops.lib()
     wl = W.generate(args.config)

@@ -2,7 +2,8 @@
  * pagedkv.h -- C ABI of libpagedkv.so, the PagedAttention hot path for AMD
  * Instinct MI355X (gfx950, CDNA4).
  *
- * The problem these calls solve is stated on the pages this library follows:
+ * The problem these calls solve is stated on the pages this library follows
+ * (each call below cites its own passage):
  *   - gaoleia.github.io "PagedAttention 和 Continuous Batching": §1.3 (a
  *     physical block holds block_size tokens of K and of V, each token a
  *     [num_heads, head_dim] row), §1.4 (a per-request block table maps
@@ -14,7 +15,8 @@
  *     a new token's K/V at its in-block position).
  *
  * Conventions shared by every call
- *   Memory.   Every pointer argument is a DEVICE pointer owned by the caller;
+ *   Memory.   Every pointer argument is a DEVICE pointer owned by the caller
+ *             (pkv_swap_blocks also takes pinned host memory);
  *             the library allocates and frees nothing and keeps no state
  *             other than a thread-local error string and process-wide tuning
  *             knobs.  Buffers must stay alive until the enqueued work ends.
@@ -188,6 +190,43 @@ int pkv_paged_attention_varlen(float* out, const void* query, const void* key_ca
                                int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
                                int32_t block_size, float scale, pkv_dtype dtype, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/*
+ * Copy-on-write block copies inside the pools (lakecityint.com/news/209622
+ * §3.2: before a sequence writes into a block other tables share, a fresh
+ * block receives a copy of it and the writer's table is pointed there).
+ *   For every pair i, block block_mapping[i][1] of key_cache becomes a bit
+ *   copy of block block_mapping[i][0], and the same in value_cache.
+ *   key_cache, value_cache  pools [num_blocks, ...] (device, read and written)
+ *   block_mapping  int64 [num_pairs][2] (src, dst)     (device, read)
+ *   block_bytes    bytes of one block of one pool (block_size * num_kv_heads
+ *                  * head_dim * element size); a multiple of 16.
+ *   Pairs with an id outside [0, num_blocks) are skipped.  Destinations must
+ *   be distinct and no destination may also be a source of the same call
+ *   (otherwise the result is unspecified).  num_pairs may be 0.
+ */
+int pkv_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping, int32_t num_pairs,
+                    int64_t num_blocks, int64_t block_bytes, void* stream);
+
+/*
+ * Swap blocks between two pools, typically a GPU pool and a pinned host pool
+ * (5688vip.com "vLLM核心机制" §3.3 and lakecityint §2.1: a preempted
+ * sequence's blocks are moved to CPU memory and later brought back, possibly
+ * into other physical blocks).
+ *   For every pair i, block block_mapping[i][1] of dst_key (dst_value) becomes
+ *   a bit copy of block block_mapping[i][0] of src_key (src_value).
+ *   Each pool pointer is device memory of the current device or pinned host
+ *   memory (hipHostMalloc, or a pinned torch tensor); pageable host memory is
+ *   rejected with PKV_EINVAL.  src_value and dst_value may both be NULL (one
+ *   pool is moved).  block_mapping is device or pinned host memory.
+ *   Pairs with a src id outside [0, src_num_blocks) or a dst id outside
+ *   [0, dst_num_blocks) are skipped; destinations must be distinct.
+ *   One kernel moves every pair (host memory is accessed over PCIe through
+ *   the device's mapping of it).
+ */
+int pkv_swap_blocks(const void* src_key, const void* src_value, void* dst_key, void* dst_value,
+                    const int64_t* block_mapping, int32_t num_pairs, int64_t src_num_blocks,
+                    int64_t dst_num_blocks, int64_t block_bytes, void* stream);
 
 /*
  * Measurement and test knobs (process-wide; not needed for normal use).

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["api.hip", "cache_kernels.hip", "decode_kernels.hip", "varlen_kernels.hip", "prefill_lds_kernels.hip"]
+SOURCES = ["api.hip", "cache_kernels.hip", "decode_kernels.hip", "varlen_kernels.hip", "prefill_lds_kernels.hip",
+           "block_kernels.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -180,6 +180,71 @@ int pkv_write_new_tokens(const int32_t* block_tables, int32_t num_seqs, int32_t 
   return e == hipSuccess ? ok() : hip_fail(e, "write_new_tokens launch");
 }
 
+int pkv_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping, int32_t num_pairs,
+                    int64_t num_blocks, int64_t block_bytes, void* stream) {
+  if (num_pairs < 0 || num_blocks < 0 || block_bytes <= 0)
+    return fail(PKV_EINVAL, "bad size (pairs %d, blocks %lld, block_bytes %lld)", num_pairs,
+                (long long)num_blocks, (long long)block_bytes);
+  if (block_bytes % 16) return fail(PKV_EINVAL, "block_bytes %lld is not a multiple of 16", (long long)block_bytes);
+  if (num_pairs == 0) return ok();
+  if (!key_cache || !value_cache || !block_mapping) return fail(PKV_EINVAL, "null pointer");
+  if (!aligned16(key_cache) || !aligned16(value_cache)) return fail(PKV_EINVAL, "pools must be 16-byte aligned");
+  hipError_t e = pkv::launch_block_copy(key_cache, key_cache, value_cache, value_cache, block_mapping, num_pairs,
+                                        num_blocks, num_blocks, block_bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "copy_blocks launch");
+}
+
+// Device address of `p` for a kernel on the current device: device memory of
+// that device, or pinned host memory (through its device mapping).  Returns
+// false for pageable host memory or another device's memory.
+static bool kernel_address(const void* p, const void** out, const char* name) {
+  hipPointerAttribute_t attr;
+  memset(&attr, 0, sizeof attr);
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();                  // do not leave the query's error for the next launch check
+    fail(PKV_EINVAL, "%s is neither device memory nor pinned host memory", name);
+    return false;
+  }
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (attr.type == hipMemoryTypeDevice && attr.device == dev) {
+    *out = p;
+    return true;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer != nullptr) {
+    *out = attr.devicePointer;
+    return true;
+  }
+  fail(PKV_EINVAL, "%s is neither memory of the current device nor pinned host memory (type %d, device %d)", name,
+       (int)attr.type, attr.device);
+  return false;
+}
+
+int pkv_swap_blocks(const void* src_key, const void* src_value, void* dst_key, void* dst_value,
+                    const int64_t* block_mapping, int32_t num_pairs, int64_t src_num_blocks,
+                    int64_t dst_num_blocks, int64_t block_bytes, void* stream) {
+  if (num_pairs < 0 || src_num_blocks < 0 || dst_num_blocks < 0 || block_bytes <= 0)
+    return fail(PKV_EINVAL, "bad size (pairs %d, blocks %lld/%lld, block_bytes %lld)", num_pairs,
+                (long long)src_num_blocks, (long long)dst_num_blocks, (long long)block_bytes);
+  if (block_bytes % 16) return fail(PKV_EINVAL, "block_bytes %lld is not a multiple of 16", (long long)block_bytes);
+  if (num_pairs == 0) return ok();
+  if (!src_key || !dst_key || !block_mapping) return fail(PKV_EINVAL, "null pointer");
+  if ((src_value == nullptr) != (dst_value == nullptr))
+    return fail(PKV_EINVAL, "src_value and dst_value must be both set or both NULL");
+  if (!aligned16(src_key) || !aligned16(dst_key) || !aligned16(src_value) || !aligned16(dst_value))
+    return fail(PKV_EINVAL, "pools must be 16-byte aligned");
+  const void *sk, *dk, *sv = nullptr, *dv = nullptr, *map;
+  if (!kernel_address(src_key, &sk, "src_key") || !kernel_address(dst_key, &dk, "dst_key") ||
+      !kernel_address(block_mapping, &map, "block_mapping"))
+    return PKV_EINVAL;
+  if (src_value && (!kernel_address(src_value, &sv, "src_value") || !kernel_address(dst_value, &dv, "dst_value")))
+    return PKV_EINVAL;
+  hipError_t e = pkv::launch_block_copy(sk, const_cast<void*>(dk), sv, const_cast<void*>(dv),
+                                        static_cast<const int64_t*>(map), num_pairs, src_num_blocks, dst_num_blocks,
+                                        block_bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "swap_blocks launch");
+}
+
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, pkv_dtype dtype) {
   if (num_seqs < 0 || num_seqs > kMaxSeqs) return 0;

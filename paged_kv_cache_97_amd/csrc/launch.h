@@ -55,6 +55,13 @@ hipError_t launch_write_tokens(const int32_t* bt, int num_seqs, int max_blocks, 
                                const void* value, void* kc, void* vc, int row_bytes, int64_t num_slots,
                                int64_t* slots, hipStream_t stream);
 
+// Whole-block copies for every (src, dst) pair of mapping (int64 [pairs][2]);
+// src1/dst1 may be null (one pool).  Pairs with an id outside its pool are
+// skipped.
+hipError_t launch_block_copy(const void* src0, void* dst0, const void* src1, void* dst1, const int64_t* mapping,
+                             int num_pairs, int64_t src_blocks, int64_t dst_blocks, int64_t block_bytes,
+                             hipStream_t stream);
+
 }  // namespace pkv
 
 namespace pkv {
@@ -87,5 +94,12 @@ size_t prefill_plan_bytes(int num_seqs);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool bf16, int cus,
                           hipStream_t stream);
 hipError_t launch_prefill_lds(const PrefillArgs& a, int block_size, int cus, hipStream_t stream);
+
+// Whole-block copies for every (src, dst) pair of mapping (int64 [pairs][2]);
+// src1/dst1 may be null (one pool).  Pairs with an id outside its pool are
+// skipped.
+hipError_t launch_block_copy(const void* src0, void* dst0, const void* src1, void* dst1, const int64_t* mapping,
+                             int num_pairs, int64_t src_blocks, int64_t dst_blocks, int64_t block_bytes,
+                             hipStream_t stream);
 
 }  // namespace pkv

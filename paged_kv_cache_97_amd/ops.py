@@ -36,6 +36,8 @@ _SIGNATURES = {
     "pkv_paged_attention_varlen": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,
                                             _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
                                             _c_f32, _c_i32, _c_vp, _c_sz, _c_vp]),
+    "pkv_copy_blocks": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp]),
+    "pkv_swap_blocks": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_vp]),
     "pkv_set_profile_events": (_c_i32, [_c_vp, _c_vp]),
     "pkv_set_decode_workers": (_c_i32, [_c_i32]),
     "pkv_set_waves_per_cu": (_c_i32, [_c_i32]),
@@ -224,6 +226,61 @@ def paged_attention_varlen(query: torch.Tensor, key_cache: torch.Tensor, value_c
         Hq, Hkv, D, NB, bs, float(scale), _kv_dtype(query), _dev(ws, "workspace"),
         ws.numel() * ws.element_size(), _stream(query)), "paged_attention_varlen")
     return out
+
+
+# ----------------------------------------------------------------- block copies
+def _block_bytes(pool: torch.Tensor) -> int:
+    return pool[0].numel() * pool.element_size() if pool.shape[0] else 0
+
+
+def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_mapping: torch.Tensor) -> None:
+    """Copy-on-write copies: block dst of each pool becomes block src, for
+    every (src, dst) row of the int64 [N, 2] mapping (on the GPU)."""
+    if value_cache.shape != key_cache.shape or value_cache.dtype != key_cache.dtype:
+        raise ValueError("key_cache and value_cache must have one shape and dtype")
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [N, 2]")
+    _check(lib().pkv_copy_blocks(_dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+                                 _dev(block_mapping, "block_mapping", torch.int64, 2), block_mapping.shape[0],
+                                 key_cache.shape[0], _block_bytes(key_cache), _stream(key_cache)), "copy_blocks")
+
+
+def _pool_ptr(t: Optional[torch.Tensor], name: str) -> int:
+    """A GPU tensor, or a pinned CPU tensor (the library maps it)."""
+    if t is None:
+        return 0
+    if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous tensor" % name)
+    if not t.is_cuda and not t.is_pinned():
+        raise ValueError("%s must be on the GPU or in pinned host memory" % name)
+    return t.data_ptr()
+
+
+def swap_blocks(src_key: torch.Tensor, src_value: Optional[torch.Tensor], dst_key: torch.Tensor,
+                dst_value: Optional[torch.Tensor], block_mapping: torch.Tensor, device=None) -> None:
+    """Swap-out / swap-in: block dst of the dst pools becomes block src of the
+    src pools for every (src, dst) row of block_mapping.  Pools are GPU or
+    pinned CPU tensors with equal block shapes; the copy runs on ``device``
+    (the GPU side's device by default) on its current stream."""
+    pools = [p for p in (src_key, src_value, dst_key, dst_value) if p is not None]
+    if any(p.shape[1:] != src_key.shape[1:] or p.dtype != src_key.dtype for p in pools):
+        raise ValueError("pools must share block shape and dtype")
+    if (src_value is None) != (dst_value is None):
+        raise ValueError("src_value and dst_value must be both given or both None")
+    if src_value is not None and (src_value.shape != src_key.shape or dst_value.shape != dst_key.shape):
+        raise ValueError("key and value pools of one side must match")
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2 or block_mapping.dtype != torch.int64:
+        raise ValueError("block_mapping must be int64 [N, 2]")
+    if device is None:
+        device = next((p.device for p in pools + [block_mapping] if p.is_cuda), None)
+        if device is None:
+            raise ValueError("no GPU tensor given: pass device")
+    with torch.cuda.device(device):
+        _check(lib().pkv_swap_blocks(_pool_ptr(src_key, "src_key"), _pool_ptr(src_value, "src_value"),
+                                     _pool_ptr(dst_key, "dst_key"), _pool_ptr(dst_value, "dst_value"),
+                                     _pool_ptr(block_mapping, "block_mapping"), block_mapping.shape[0],
+                                     src_key.shape[0], dst_key.shape[0], _block_bytes(src_key),
+                                     torch.cuda.current_stream(device).cuda_stream), "swap_blocks")
 
 
 # ----------------------------------------------------------------- knobs and timing

@@ -92,3 +92,17 @@ def test_workspace_size_rules():
     assert lib.pkv_set_decode_workers(-5) == -1
     assert lib.pkv_set_waves_per_cu(5) == -1
     assert lib.pkv_set_profile_events(ctypes.c_void_p(1), None) == 1
+
+
+def test_block_copy_validation():
+    lib = ops.lib()
+    assert lib.pkv_copy_blocks(None, None, None, 0, 10, 4096, None) == 0          # no pairs: nothing enqueued
+    assert lib.pkv_copy_blocks(None, None, None, 2, 10, 4096, None) == 1          # null pointers
+    assert lib.pkv_copy_blocks(None, None, None, -1, 10, 4096, None) == 1
+    assert lib.pkv_copy_blocks(None, None, None, 2, 10, 4100, None) == 1          # not a multiple of 16
+    assert lib.pkv_swap_blocks(None, None, None, None, None, 0, 4, 4, 4096, None) == 0
+    assert lib.pkv_swap_blocks(None, None, None, None, None, 3, 4, 4, 4096, None) == 1
+    assert lib.pkv_swap_blocks(ctypes.c_void_p(256), ctypes.c_void_p(512), ctypes.c_void_p(768), None,
+                               ctypes.c_void_p(1024), 3, 4, 4, 4096, None) == 1   # one value pool only
+    assert lib.pkv_swap_blocks(None, None, None, None, None, 3, 4, -4, 4096, None) == 1
+    assert lib.pkv_last_error()
