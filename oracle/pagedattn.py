@@ -21,6 +21,14 @@ What it computes, and where the pages state it:
     write: a new physical block receives a copy of the shared block before
     one sharer writes) and §2.1, 5688vip.com "vLLM核心机制" §3.3 (preemption
     swaps a sequence's blocks out to CPU memory and back in later).
+  * FP8 KV cache -- feifeigd "vLLM 架构详解" 三 生产级部署配置, 关键参数调优
+    (kv-cache-dtype auto or fp8: fp8 halves KV memory at a small loss of
+    precision).  The pages name no format or scale; the reading taken here is
+    OCP FP8 E4M3 (bias 7, no infinities, S.1111.111 is NaN, largest finite
+    448, subnormals m/8 * 2^-6) with one float scale per pool: a value x is
+    stored as the E4M3 code nearest to float32(x) * float32(1 / scale) (ties
+    to the even code, magnitudes past 448 saturate to 448) and read back as
+    E4M3 value * scale.
   * varlen rows -- gaoleia §2.4 (one iteration mixes decode rows and prefill
     rows) and §2.5 (a long prompt is cut into 512-token chunks interleaved
     with decodes); fanquanpp.github.io "vLLM服务内部" 分块预填充.  A chunk of q
@@ -44,6 +52,7 @@ __all__ = [
     "to_f64", "slot_mapping", "reshape_and_cache", "gather_tokens",
     "decode_attention", "varlen_attention", "attention_rows",
     "partial_attention", "combine_partials", "copy_blocks", "swap_blocks",
+    "e4m3_value", "e4m3_encode", "quantize_kv", "reshape_and_cache_fp8",
 ]
 
 
@@ -141,10 +150,19 @@ def attention_rows(q, k, v, scale, visible):
     return out
 
 
-def decode_attention(query, key_cache, value_cache, block_tables, seq_lens, scale, dtype):
+def _kv_rows(cache, table_row, length, block_size, dtype, kv_scale):
+    rows = gather_tokens(cache, table_row, length, block_size)
+    if kv_scale is None:
+        return to_f64(rows, dtype)
+    return e4m3_value(rows) * float(kv_scale)
+
+
+def decode_attention(query, key_cache, value_cache, block_tables, seq_lens, scale, dtype, kv_scales=None):
     """One query row per sequence over its first seq_lens[s] cached tokens.
 
     query [B, Hq, D]; caches [NB, bs, Hkv, D]; returns float64 [B, Hq, D].
+    kv_scales = (k_scale, v_scale) means the caches hold E4M3 codes, read as
+    code value * scale; the query stays in `dtype`.
     """
     B, Hq, D = query.shape
     Hkv = key_cache.shape[2]
@@ -156,8 +174,9 @@ def decode_attention(query, key_cache, value_cache, block_tables, seq_lens, scal
         L = int(seq_lens[s])
         if L == 0:
             continue
-        k = to_f64(gather_tokens(key_cache, block_tables[s], L, bs), dtype)
-        v = to_f64(gather_tokens(value_cache, block_tables[s], L, bs), dtype)
+        ks, vs = kv_scales if kv_scales is not None else (None, None)
+        k = _kv_rows(key_cache, block_tables[s], L, bs, dtype, ks)
+        v = _kv_rows(value_cache, block_tables[s], L, bs, dtype, vs)
         q = to_f64(query[s], dtype)
         for h in range(Hq):
             g = h // group
@@ -165,12 +184,14 @@ def decode_attention(query, key_cache, value_cache, block_tables, seq_lens, scal
     return out
 
 
-def varlen_attention(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, scale, dtype):
+def varlen_attention(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, scale, dtype,
+                     kv_scales=None):
     """Mixed prefill-chunk and decode rows in one step.
 
     Sequence s owns rows qsl[s]..qsl[s+1]-1 (q_s of them); row i sits at
     position seq_lens[s] - q_s + i and attends keys 0..that position.
-    query [T, Hq, D]; returns float64 [T, Hq, D].
+    query [T, Hq, D]; returns float64 [T, Hq, D].  kv_scales as in
+    decode_attention.
     """
     T, Hq, D = query.shape
     Hkv = key_cache.shape[2]
@@ -187,8 +208,9 @@ def varlen_attention(query, key_cache, value_cache, block_tables, seq_lens, quer
         L = int(seq_lens[s])
         assert L >= nq, "fewer keys than query rows"
         visible = [L - nq + i + 1 for i in range(nq)]
-        k = to_f64(gather_tokens(key_cache, block_tables[s], L, bs), dtype)
-        v = to_f64(gather_tokens(value_cache, block_tables[s], L, bs), dtype)
+        ks, vs = kv_scales if kv_scales is not None else (None, None)
+        k = _kv_rows(key_cache, block_tables[s], L, bs, dtype, ks)
+        v = _kv_rows(value_cache, block_tables[s], L, bs, dtype, vs)
         q = to_f64(query[r0:r1], dtype)
         for h in range(Hq):
             g = h // group
@@ -246,3 +268,50 @@ def swap_blocks(src_pool, dst_pool, mapping):
     for src, dst in pairs:
         out[dst] = src_pool[src]
     return out
+
+
+# ---------------------------------------------------------------- FP8 (OCP E4M3)
+def e4m3_value(codes) -> np.ndarray:
+    """Value of each E4M3 byte as float64 (NaN for S.1111.111)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+_E4M3_POS = e4m3_value(np.arange(0x7F))          # codes 0x00..0x7E, increasing magnitudes
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Nearest E4M3 code of each float (ties to the even code; magnitudes of
+    448 and more give 448).  Inputs must not be NaN."""
+    v = np.asarray(v, dtype=np.float64)
+    assert not np.isnan(v).any(), "NaN has no saturating code"
+    a = np.minimum(np.abs(v), 448.0)
+    hi = np.searchsorted(_E4M3_POS, a, side="left")          # first code with value >= a
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(a == _E4M3_POS[hi], hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    return np.where(np.signbit(v), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def quantize_kv(x, dtype, kv_scale) -> np.ndarray:
+    """E4M3 codes of stored values x (bf16 bits or float32): the float32
+    product of x and the float32 reciprocal of the scale, rounded once."""
+    inv = np.float32(1.0) / np.float32(kv_scale)
+    xf = to_f64(x, dtype).astype(np.float32)
+    return e4m3_encode((xf * inv).astype(np.float32))
+
+
+def reshape_and_cache_fp8(key, value, key_cache, value_cache, slots, k_scale, v_scale, dtype, ref_counts=None):
+    """reshape_and_cache into E4M3 pools: each new token's K and V rows are
+    quantised (quantize_kv) and stored at its slot; nothing else changes."""
+    kq = quantize_kv(key, dtype, k_scale)
+    vq = quantize_kv(value, dtype, v_scale)
+    return reshape_and_cache(kq, vq, key_cache, value_cache, slots, ref_counts)

@@ -517,3 +517,98 @@ def test_cow_pins_catch_planted_mistakes():
     assert not np.array_equal(skip[0][0], _logical_attention(sc, 0, 0))
     _, _, konly = _run_scenario_oracle(sc, k_only=True)
     assert not np.array_equal(konly[0][0], _logical_attention(sc, 0, 0))
+
+
+# ---------------------------------------------------------------- P10 FP8 (OCP E4M3) KV cache
+def _torch_e4m3_value(codes):
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def _torch_e4m3_code(v):
+    return torch.from_numpy(np.asarray(v, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_values_match_the_format_and_torch():
+    v = oracle.e4m3_value(np.arange(256))
+    t = _torch_e4m3_value(np.arange(256))
+    assert np.array_equal(np.isnan(v), np.isnan(t)) and np.array_equal(v[~np.isnan(v)], t[~np.isnan(t)])
+    # fixed points of the format: 1.0, largest normal, smallest normal and subnormal, NaN, -0
+    assert v[0x38] == 1.0 and v[0x7E] == 448.0 and v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and v[0x80] == 0.0 and np.signbit(v[0x80])
+    assert np.all(np.diff(v[:0x7F]) > 0)                      # magnitudes increase with the code
+
+
+def test_e4m3_encode_rounds_to_nearest_even_like_torch():
+    rng = np.random.default_rng(101)
+    pos = oracle.e4m3_value(np.arange(0x7F))
+    mids = (pos[:-1] + pos[1:]) / 2                            # exact ties (representable in float32)
+    near = np.concatenate([np.nextafter(mids.astype(np.float32), np.float32(0)),
+                           np.nextafter(mids.astype(np.float32), np.float32(1e9))])
+    x = np.concatenate([rng.standard_normal(20000) * 40, rng.standard_normal(2000) * 1e-3, mids, -mids, near,
+                        -near, pos, -pos, [0.0, 447.9, 448.0, 460.0]]).astype(np.float32)
+    got = oracle.e4m3_encode(x)
+    assert np.array_equal(got, _torch_e4m3_code(x))
+    # ties go to the even code: halfway between 1.0 (0x38) and 1.125 (0x39) -> 0x38;
+    # halfway between 1.125 and 1.25 (0x3A) -> 0x3A
+    assert oracle.e4m3_encode([1.0625, 1.1875])[0] == 0x38 and oracle.e4m3_encode([1.1875])[0] == 0x3A
+    # saturation (torch turns these into NaN; the reading here saturates)
+    assert list(oracle.e4m3_encode([464.0, 1e6, -1e6, -500.0])) == [0x7E, 0x7E, 0xFE, 0xFE]
+    # every finite code survives a round trip
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    assert np.array_equal(oracle.e4m3_encode(oracle.e4m3_value(finite)), np.array(finite, np.uint8))
+
+
+def test_quantize_kv_is_one_float32_product_then_one_rounding():
+    rng = np.random.default_rng(102)
+    x = rng.standard_normal(50000).astype(np.float32)
+    bits = W._to_bf16_bits(x)
+    for scale in (0.0125, 1.0 / 64, 0.37):
+        inv = torch.tensor(1.0, dtype=torch.float32) / torch.tensor(scale, dtype=torch.float32)
+        xf = torch.from_numpy(bits.astype(np.int32) << 16).view(torch.float32)
+        ref = (xf * inv).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(oracle.quantize_kv(bits, "bf16", scale), ref)
+        assert np.array_equal(oracle.quantize_kv(x, "f32", scale),
+                              (torch.from_numpy(x) * inv).clamp(-448, 448).to(torch.float8_e4m3fn)
+                              .view(torch.uint8).numpy())
+
+
+def test_fp8_attention_equals_attention_over_dequantised_pools():
+    """Decode over E4M3 pools with power-of-two scales equals, bit for bit,
+    decode over float32 pools holding torch's decoding of the same codes times
+    the scales; swapping the two scales is caught."""
+    wl = W.generate(SMALL_DECODE, seed=103)
+    _, kc, vc = _after_write(wl)
+    ks, vs = 1.0 / 64, 1.0 / 32
+    kq = oracle.quantize_kv(np.where(kc == W.BF16_NAN, 0, kc).astype(np.uint16), "bf16", ks)
+    vq = oracle.quantize_kv(np.where(vc == W.BF16_NAN, 0, vc).astype(np.uint16), "bf16", vs)
+    got = oracle.decode_attention(wl.query, kq, vq, wl.block_tables, wl.seq_lens, wl.scale, "bf16", (ks, vs))
+    kf = (_torch_e4m3_value(kq) * ks).astype(np.float32)
+    vf = (_torch_e4m3_value(vq) * vs).astype(np.float32)
+    q32 = oracle.to_f64(wl.query, "bf16").astype(np.float32)
+    ref = oracle.decode_attention(q32, kf, vf, wl.block_tables, wl.seq_lens, wl.scale, "f32")
+    assert np.array_equal(got, ref)
+    swapped = oracle.decode_attention(wl.query, kq, vq, wl.block_tables, wl.seq_lens, wl.scale, "bf16", (vs, ks))
+    assert not np.allclose(got, swapped)
+
+
+def test_fp8_write_then_decode_equals_dense_attention_of_dequantised_tokens():
+    wl = W.generate(SMALL_DECODE, seed=104, keep_logical=True)
+    ks, vs = 0.0125, 0.02
+    slots = oracle.slot_mapping(wl.block_tables, wl.positions, wl.query_start_loc, wl.spec.block_size, wl.num_blocks)
+    kc0 = np.full(wl.key_cache.shape, 0xFF, np.uint8)            # E4M3 NaN in every slot ...
+    vc0 = np.full(wl.value_cache.shape, 0xFF, np.uint8)
+    live = wl.key_cache != W.BF16_NAN                              # ... except cached tokens
+    kc0[live] = oracle.quantize_kv(wl.key_cache[live], "bf16", ks)
+    vc0[live] = oracle.quantize_kv(wl.value_cache[live], "bf16", vs)
+    kc, vc = oracle.reshape_and_cache_fp8(wl.key, wl.value, kc0, vc0, slots, ks, vs, "bf16", wl.ref_counts)
+    changed = np.any(kc != kc0, axis=(2, 3)) | np.any(vc != vc0, axis=(2, 3))
+    written = {(int(s) // wl.spec.block_size, int(s) % wl.spec.block_size) for s in slots if s >= 0}
+    assert {tuple(x) for x in np.argwhere(changed)} <= written
+    got = oracle.decode_attention(wl.query, kc, vc, wl.block_tables, wl.seq_lens, wl.scale, "bf16", (ks, vs))
+    G = wl.spec.num_q_heads // wl.spec.num_kv_heads
+    for s in range(wl.num_seqs):
+        L = int(wl.seq_lens[s])
+        k = oracle.e4m3_value(oracle.quantize_kv(wl.logical_k[s][:L], "bf16", ks)) * ks
+        v = oracle.e4m3_value(oracle.quantize_kv(wl.logical_v[s][:L], "bf16", vs)) * vs
+        ref = _sdpa_reference(oracle.to_f64(wl.query[s:s + 1], "bf16"), k, v, wl.scale, [L], G)[0]
+        np.testing.assert_allclose(got[s], ref, rtol=0, atol=1e-12)
