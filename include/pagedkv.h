@@ -39,7 +39,10 @@
  *             a sequence's last block are ignored (pad them with -1).
  *   Types.    dtype PKV_BF16 means query/key/value/caches hold bfloat16,
  *             PKV_F32 float32; outputs are always float32; accumulation is
- *             float32.  Pointers to data must be 16-byte aligned.
+ *             float32.  PKV_FP8_E4M3 pools (the *_fp8 calls) hold one OCP
+ *             E4M3 byte per element with one float scale per pool, while
+ *             query/key/value stay bfloat16 (key/value may also be float32).
+ *             Pointers to data must be 16-byte aligned.
  *   GQA.      Query head hq reads KV head hq / (num_q_heads / num_kv_heads).
  *   Support.  head_dim in {64, 128}; block_size in {16, 32};
  *             num_q_heads % num_kv_heads == 0.  Other values return
@@ -55,7 +58,7 @@
 extern "C" {
 #endif
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
 
 typedef enum {
   PKV_OK = 0,
@@ -126,9 +129,38 @@ int pkv_write_new_tokens(const int32_t* block_tables, int32_t num_seqs, int32_t 
                          pkv_dtype dtype, int64_t* slot_mapping, void* stream);
 
 /*
+ * FP8 KV cache (feifeigd "vLLM 架构详解" 三 生产级部署配置, 关键参数调优:
+ * kv-cache-dtype fp8 halves KV-cache memory at a small loss of precision).
+ * The pages fix neither format nor scaling; these calls use OCP FP8 E4M3
+ * (bias 7, no infinities, largest finite 448) with one float scale per pool.
+ * An element x is stored as the E4M3 code nearest to the float32 product
+ * x * (1.0f / scale) -- the reciprocal rounded to float32 on the host, ties to
+ * the even code, magnitudes beyond 448 saturating to +-448 -- and read back as
+ * code value * scale.  key/value must be finite.
+ *
+ * pkv_reshape_and_cache_fp8 / pkv_write_new_tokens_fp8: as pkv_reshape_and_cache
+ * / pkv_write_new_tokens, with key/value of in_dtype (PKV_BF16 or PKV_F32)
+ * [num_tokens, num_kv_heads, head_dim] and key_cache/value_cache uint8
+ * [num_blocks, block_size, num_kv_heads, head_dim] (E4M3 codes).
+ * num_kv_heads * head_dim must be a multiple of 16.  k_scale and v_scale must
+ * be positive and finite with finite reciprocals (else PKV_EINVAL).
+ */
+int pkv_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache, void* value_cache,
+                              const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                              int32_t head_dim, int64_t num_blocks, int32_t block_size, pkv_dtype in_dtype,
+                              float k_scale, float v_scale, void* stream);
+int pkv_write_new_tokens_fp8(const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                             const int32_t* positions, const int32_t* query_start_loc, int32_t num_tokens,
+                             int32_t block_size, const void* key, const void* value, void* key_cache,
+                             void* value_cache, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                             pkv_dtype in_dtype, float k_scale, float v_scale, int64_t* slot_mapping,
+                             void* stream);
+
+/*
  * Bytes of device workspace pkv_paged_attention_decode needs for this shape
  * on the CURRENT device (the split of the work depends on its compute-unit
- * count).  Returns 0 for shapes the library does not support.
+ * count).  Returns 0 for shapes the library does not support.  dtype is the
+ * pool type (PKV_FP8_E4M3 for pkv_paged_attention_decode_fp8).
  */
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, pkv_dtype dtype);
@@ -157,6 +189,22 @@ int pkv_paged_attention_decode(float* out, const void* query, const void* key_ca
                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
                                pkv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode attention over E4M3 pools: pkv_paged_attention_decode with query
+ * bfloat16 [num_seqs, num_q_heads, head_dim], key_cache/value_cache uint8
+ * E4M3 codes, and every K element read as code value * k_scale, every V
+ * element as code value * v_scale (the scales of the write).  Tiles are
+ * widened to bfloat16 exactly in registers; k_scale is folded into `scale`
+ * and v_scale into the final normalisation.  Workspace as for
+ * pkv_decode_workspace_size(..., PKV_FP8_E4M3).
+ */
+int pkv_paged_attention_decode_fp8(float* out, const void* query, const void* key_cache, const void* value_cache,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
+                                   float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /*
  * Bytes of device workspace pkv_paged_attention_varlen needs (current device).
@@ -190,6 +238,20 @@ int pkv_paged_attention_varlen(float* out, const void* query, const void* key_ca
                                int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
                                int32_t block_size, float scale, pkv_dtype dtype, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/*
+ * Varlen attention over E4M3 pools: pkv_paged_attention_varlen with the pool
+ * conventions of pkv_paged_attention_decode_fp8 (query bfloat16, pools E4M3
+ * codes read as code value * k_scale / v_scale).  Workspace as for
+ * pkv_varlen_workspace_size(..., PKV_FP8_E4M3).
+ */
+int pkv_paged_attention_varlen_fp8(float* out, const void* query, const void* key_cache, const void* value_cache,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                   const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                                   int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t block_size,
+                                   float scale, float k_scale, float v_scale, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /*
  * Copy-on-write block copies inside the pools (lakecityint.com/news/209622

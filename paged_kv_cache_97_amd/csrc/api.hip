@@ -68,9 +68,23 @@ int check_shape(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int
     return fail(PKV_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
   if (block_size != 16 && block_size != 32)
     return fail(PKV_EUNSUPPORTED, "block_size %d (supported: 16, 32)", block_size);
-  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "dtype %d", (int)dtype);
+  if (dtype != PKV_F32 && dtype != PKV_BF16 && dtype != PKV_FP8_E4M3)
+    return fail(PKV_EUNSUPPORTED, "dtype %d", (int)dtype);
   return PKV_OK;
 }
+
+// Pool format of an attention call: element kind and, for E4M3 pools, the
+// two scales (1 otherwise).
+struct KvFormat {
+  pkv::KvKind kind;
+  float k_scale;
+  float v_scale;
+};
+
+KvFormat plain_format(pkv_dtype dt) { return {dt == PKV_BF16 ? pkv::KvKind::BF16 : pkv::KvKind::F32, 1.f, 1.f}; }
+
+// A pool scale must be positive and finite with a finite float32 reciprocal.
+bool good_scale(float s) { return std::isfinite(s) && s > 0.f && std::isfinite(1.0f / s); }
 
 // Upper bound of the chunk count the split sees, times the worker count, must
 // stay far inside int64 (the kernels multiply the two).
@@ -180,6 +194,61 @@ int pkv_write_new_tokens(const int32_t* block_tables, int32_t num_seqs, int32_t 
   return e == hipSuccess ? ok() : hip_fail(e, "write_new_tokens launch");
 }
 
+static int check_fp8_write(int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                           int32_t block_size, pkv_dtype in_dtype, float k_scale, float v_scale) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks < 0 || block_size <= 0)
+    return fail(PKV_EINVAL, "bad size (tokens %d, kv_heads %d, head_dim %d, blocks %lld, block_size %d)",
+                num_tokens, num_kv_heads, head_dim, (long long)num_blocks, block_size);
+  if (in_dtype != PKV_F32 && in_dtype != PKV_BF16)
+    return fail(PKV_EUNSUPPORTED, "key/value dtype %d (bf16 or f32)", (int)in_dtype);
+  if (((int64_t)num_kv_heads * head_dim) % 16)
+    return fail(PKV_EUNSUPPORTED, "token row of %lld elements is not a multiple of 16",
+                (long long)num_kv_heads * head_dim);
+  if (!good_scale(k_scale) || !good_scale(v_scale))
+    return fail(PKV_EINVAL, "k_scale %g / v_scale %g must be positive and finite", k_scale, v_scale);
+  return PKV_OK;
+}
+
+int pkv_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache, void* value_cache,
+                              const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                              int32_t head_dim, int64_t num_blocks, int32_t block_size, pkv_dtype in_dtype,
+                              float k_scale, float v_scale, void* stream) {
+  int st = check_fp8_write(num_tokens, num_kv_heads, head_dim, num_blocks, block_size, in_dtype, k_scale, v_scale);
+  if (st != PKV_OK) return st;
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return fail(PKV_EINVAL, "null pointer");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PKV_EINVAL, "key/value/cache pointers must be 16-byte aligned");
+  hipError_t e = pkv::launch_reshape_and_cache_fp8(
+      key, value, key_cache, value_cache, slot_mapping, num_tokens, num_kv_heads * head_dim, num_blocks * block_size,
+      in_dtype == PKV_BF16 ? pkv::KvKind::BF16 : pkv::KvKind::F32, 1.0f / k_scale, 1.0f / v_scale,
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "reshape_and_cache_fp8 launch");
+}
+
+int pkv_write_new_tokens_fp8(const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                             const int32_t* positions, const int32_t* query_start_loc, int32_t num_tokens,
+                             int32_t block_size, const void* key, const void* value, void* key_cache,
+                             void* value_cache, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                             pkv_dtype in_dtype, float k_scale, float v_scale, int64_t* slot_mapping, void* stream) {
+  int st = check_fp8_write(num_tokens, num_kv_heads, head_dim, num_blocks, block_size, in_dtype, k_scale, v_scale);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || max_blocks_per_seq < 0)
+    return fail(PKV_EINVAL, "negative size (seqs %d, max_blocks %d)", num_seqs, max_blocks_per_seq);
+  if (num_tokens == 0) return ok();
+  if (!positions || !query_start_loc || !key || !value || !key_cache || !value_cache ||
+      (num_seqs > 0 && max_blocks_per_seq > 0 && !block_tables))
+    return fail(PKV_EINVAL, "null pointer");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PKV_EINVAL, "key/value/cache pointers must be 16-byte aligned");
+  hipError_t e = pkv::launch_write_tokens_fp8(
+      block_tables, num_seqs, max_blocks_per_seq, positions, query_start_loc, num_tokens, block_size, key, value,
+      key_cache, value_cache, num_kv_heads * head_dim, num_blocks * block_size, slot_mapping,
+      in_dtype == PKV_BF16 ? pkv::KvKind::BF16 : pkv::KvKind::F32, 1.0f / k_scale, 1.0f / v_scale,
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "write_new_tokens_fp8 launch");
+}
+
 int pkv_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping, int32_t num_pairs,
                     int64_t num_blocks, int64_t block_bytes, void* stream) {
   if (num_pairs < 0 || num_blocks < 0 || block_bytes <= 0)
@@ -257,7 +326,7 @@ static int run_decode(float* out, const void* query, const void* key_cache, cons
                       const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
                       const int32_t* qsl, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t max_seq_len,
-                      float scale, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                      float scale, KvFormat fmt, void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
   const int group = num_q_heads / num_kv_heads;
   const int workers = decode_workers();
@@ -285,20 +354,20 @@ static int run_decode(float* out, const void* query, const void* key_cache, cons
   a.head_tiles = head_tiles;
   a.tile_cols = group < 16 ? group : 16;
   a.num_blocks = num_blocks;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.scale_log2 = scale * fmt.k_scale * 1.4426950408889634f;
+  a.v_scale = fmt.v_scale;
   a.workers = workers;
   pkv::decode_workspace_carve(a, workspace, head_dim);
   (void)max_seq_len;
-  hipError_t e = pkv::launch_decode(a, head_dim, block_size, dtype == PKV_BF16, stream, g_ev_start, g_ev_stop);
+  hipError_t e = pkv::launch_decode(a, head_dim, block_size, fmt.kind, stream, g_ev_start, g_ev_stop);
   return e == hipSuccess ? ok() : hip_fail(e, "decode launch");
 }
 
-int pkv_paged_attention_decode(float* out, const void* query, const void* key_cache,
-                               const void* value_cache, const int32_t* block_tables,
-                               int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
-                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                               int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
-                               pkv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+static int decode_impl(float* out, const void* query, const void* key_cache, const void* value_cache,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale, pkv_dtype dtype,
+                       KvFormat fmt, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || num_seqs > kMaxSeqs) return fail(PKV_EUNSUPPORTED, "num_seqs %d (max %d)", num_seqs, kMaxSeqs);
@@ -313,7 +382,34 @@ int pkv_paged_attention_decode(float* out, const void* query, const void* key_ca
   if (max_blocks_per_seq > 0 && num_blocks == 0) return fail(PKV_EINVAL, "empty pool with a non-empty block table");
   return run_decode(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens, nullptr,
                     num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_seq_len,
-                    scale, dtype, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+                    scale, fmt, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int pkv_paged_attention_decode(float* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
+                               pkv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype == PKV_FP8_E4M3)
+    return fail(PKV_EINVAL, "E4M3 pools need their scales: use pkv_paged_attention_decode_fp8");
+  return decode_impl(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_seq_len, scale, dtype,
+                     plain_format(dtype), workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attention_decode_fp8(float* out, const void* query, const void* key_cache, const void* value_cache,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
+                                   float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (!good_scale(k_scale) || !good_scale(v_scale))
+    return fail(PKV_EINVAL, "k_scale %g / v_scale %g must be positive and finite", k_scale, v_scale);
+  return decode_impl(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_seq_len, scale,
+                     PKV_FP8_E4M3, KvFormat{pkv::KvKind::FP8, k_scale, v_scale}, workspace, workspace_bytes,
+                     stream);
 }
 
 static size_t varlen_decode_part(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
@@ -332,14 +428,12 @@ size_t pkv_varlen_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
   return varlen_decode_part(num_seqs, num_q_heads, num_kv_heads, head_dim) + pkv::prefill_plan_bytes(num_seqs);
 }
 
-int pkv_paged_attention_varlen(float* out, const void* query, const void* key_cache,
-                               const void* value_cache, const int32_t* block_tables,
-                               int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                               const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
-                               int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
-                               int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
-                               int32_t block_size, float scale, pkv_dtype dtype, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+static int varlen_impl(float* out, const void* query, const void* key_cache, const void* value_cache,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                       const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                       int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int64_t num_blocks, int32_t block_size, float scale, pkv_dtype dtype, KvFormat fmt,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || num_seqs > kMaxSeqs) return fail(PKV_EUNSUPPORTED, "num_seqs %d (max %d)", num_seqs, kMaxSeqs);
@@ -382,11 +476,12 @@ int pkv_paged_attention_varlen(float* out, const void* query, const void* key_ca
     p.num_kv_heads = num_kv_heads;
     p.group = group;
     p.num_blocks = num_blocks;
-    p.scale_log2 = scale * 1.4426950408889634f;
+    p.scale_log2 = scale * fmt.k_scale * 1.4426950408889634f;
+    p.v_scale = fmt.v_scale;
     const int cus = current_cus();
     p.waves = (cus > 0 ? cus : 256) * 4;
     p.plan = reinterpret_cast<int*>(static_cast<char*>(workspace) + dec_bytes);
-    hipError_t e = pkv::launch_prefill(p, head_dim, block_size, dtype == PKV_BF16, cus, s);
+    hipError_t e = pkv::launch_prefill(p, head_dim, block_size, fmt.kind, cus, s);
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
   }
   if (g_ev_stop) (void)hipEventRecord(g_ev_stop, s);
@@ -396,10 +491,41 @@ int pkv_paged_attention_varlen(float* out, const void* query, const void* key_ca
   g_ev_stop = nullptr;
   int rc = run_decode(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens,
                       query_start_loc, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
-                      max_seq_len, scale, dtype, workspace, workspace_bytes, s);
+                      max_seq_len, scale, fmt, workspace, workspace_bytes, s);
   g_ev_start = e0;
   g_ev_stop = e1;
   return rc;
+}
+
+int pkv_paged_attention_varlen(float* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                               const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                               int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                               int32_t block_size, float scale, pkv_dtype dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (dtype == PKV_FP8_E4M3)
+    return fail(PKV_EINVAL, "E4M3 pools need their scales: use pkv_paged_attention_varlen_fp8");
+  return varlen_impl(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens,
+                     query_start_loc, num_seqs, num_tokens, max_query_len, max_seq_len, num_q_heads, num_kv_heads,
+                     head_dim, num_blocks, block_size, scale, dtype, plain_format(dtype), workspace,
+                     workspace_bytes, stream);
+}
+
+int pkv_paged_attention_varlen_fp8(float* out, const void* query, const void* key_cache, const void* value_cache,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                   const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                                   int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t block_size,
+                                   float scale, float k_scale, float v_scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!good_scale(k_scale) || !good_scale(v_scale))
+    return fail(PKV_EINVAL, "k_scale %g / v_scale %g must be positive and finite", k_scale, v_scale);
+  return varlen_impl(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens,
+                     query_start_loc, num_seqs, num_tokens, max_query_len, max_seq_len, num_q_heads, num_kv_heads,
+                     head_dim, num_blocks, block_size, scale, PKV_FP8_E4M3,
+                     KvFormat{pkv::KvKind::FP8, k_scale, v_scale}, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

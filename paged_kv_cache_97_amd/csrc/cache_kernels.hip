@@ -10,6 +10,12 @@
 //
 // Both kernels are pure data movement bounded by launch latency at serving
 // sizes; the write moves 16 bytes per lane with fully coalesced rows.
+//
+// FP8 pools (feifeigd "vLLM 架构详解" 三 生产级部署配置: kv-cache-dtype fp8
+// halves KV memory): the write stores OCP E4M3 bytes.  Each element is
+// multiplied by the host-computed float32 reciprocal of the pool's scale,
+// clamped to +-448 (the largest finite E4M3 value, so large inputs saturate),
+// and rounded to nearest-even by v_cvt_pk_fp8_f32.  Inputs must be finite.
 #include "common.h"
 #include "launch.h"
 
@@ -119,6 +125,140 @@ write_tokens_kernel(const int32_t* __restrict__ block_tables, int num_seqs, int 
     key_cache[slot * row_vecs + cvec] = k;
     value_cache[slot * row_vecs + cvec] = v;
   }
+}
+
+// ------------------------------------------------------------------ FP8 stores
+// Four floats -> four E4M3 bytes (x * inv, saturated, round to nearest even).
+__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float inv) {
+  auto q = [inv](float x) { return fminf(fmaxf(x * inv, -448.f), 448.f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q(a), q(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(q(c), q(d), w, true);
+  return (uint32_t)w;
+}
+
+// 16 E4M3 bytes from the 16 input elements of output vector `v` of a row
+// (bf16: two 16-byte input vectors, fp32: four).
+template <bool BF16IN>
+__device__ __forceinline__ u32x4 quant16(const void* in, int64_t v, float inv) {
+  u32x4 out;
+  if constexpr (BF16IN) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(in) + 2 * v;
+    const u32x4 x0 = p[0], x1 = p[1];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const u32x4& x = w < 2 ? x0 : x1;
+      const uint32_t lo = x[2 * (w & 1)], hi = x[2 * (w & 1) + 1];
+      out[w] = quant4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xFFFF0000u), __uint_as_float(hi << 16),
+                      __uint_as_float(hi & 0xFFFF0000u), inv);
+    }
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(in) + 4 * v;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f32x4 x = p[w];
+      out[w] = quant4(x[0], x[1], x[2], x[3], inv);
+    }
+  }
+  return out;
+}
+
+template <bool BF16IN>
+__global__ void __launch_bounds__(256)
+reshape_and_cache_fp8_kernel(const void* __restrict__ key, const void* __restrict__ value,
+                             u32x4* __restrict__ key_cache, u32x4* __restrict__ value_cache,
+                             const int64_t* __restrict__ slots, int64_t total, int row_vecs, int64_t num_slots,
+                             float k_inv, float v_inv) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / row_vecs;
+    const int64_t c = i - t * row_vecs;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    key_cache[slot * row_vecs + c] = quant16<BF16IN>(key, i, k_inv);
+    value_cache[slot * row_vecs + c] = quant16<BF16IN>(value, i, v_inv);
+  }
+}
+
+// write_tokens_kernel with quantising stores (same slot computation).
+template <bool BF16IN>
+__global__ void __launch_bounds__(256)
+write_tokens_fp8_kernel(const int32_t* __restrict__ block_tables, int num_seqs, int max_blocks,
+                        const int32_t* __restrict__ positions, const int32_t* __restrict__ qsl, int num_tokens,
+                        int block_size, const void* __restrict__ key, const void* __restrict__ value,
+                        u32x4* __restrict__ key_cache, u32x4* __restrict__ value_cache, int row_vecs,
+                        int64_t num_slots, int64_t* __restrict__ slots_out, float k_inv, float v_inv) {
+  __shared__ int qs[kQslLds];
+  __shared__ int64_t s_slot[kTokensPerWg];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kTokensPerWg;
+  const bool staged = num_seqs + 1 <= kQslLds;
+  if (staged)
+    for (int i = tid; i <= num_seqs; i += 256) qs[i] = qsl[i];
+  __syncthreads();
+  if (tid < kTokensPerWg) {
+    const int t = t0 + tid;
+    int64_t slot = -1;
+    if (t < num_tokens) {
+      const int32_t* q = staged ? qs : qsl;
+      int lo = 0, hi = num_seqs;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (q[mid] <= t) lo = mid; else hi = mid;
+      }
+      const int p = positions[t];
+      if (num_seqs > 0 && t < q[lo + 1] && p >= 0) {
+        const int lb = p / block_size;
+        if (lb < max_blocks) {
+          const int phys = block_tables[(int64_t)lo * max_blocks + lb];
+          if (phys >= 0) slot = (int64_t)phys * block_size + (p - lb * block_size);
+        }
+      }
+      if (slots_out) slots_out[t] = slot;
+    }
+    s_slot[tid] = slot;
+  }
+  __syncthreads();
+  const int n = min(kTokensPerWg, num_tokens - t0) * row_vecs;
+  for (int i = tid; i < n; i += 256) {
+    const int tl = i / row_vecs, cvec = i - tl * row_vecs;
+    const int64_t slot = s_slot[tl];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t src = (int64_t)(t0 + tl) * row_vecs + cvec;
+    key_cache[slot * row_vecs + cvec] = quant16<BF16IN>(key, src, k_inv);
+    value_cache[slot * row_vecs + cvec] = quant16<BF16IN>(value, src, v_inv);
+  }
+}
+
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* kc, void* vc,
+                                        const int64_t* slots, int num_tokens, int row_elems, int64_t num_slots,
+                                        KvKind in_kind, float k_inv, float v_inv, hipStream_t stream) {
+  const int row_vecs = row_elems / 16;
+  const int64_t total = (int64_t)num_tokens * row_vecs;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (in_kind == KvKind::BF16)
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, key, value,
+                       (u32x4*)kc, (u32x4*)vc, slots, total, row_vecs, num_slots, k_inv, v_inv);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, key,
+                       value, (u32x4*)kc, (u32x4*)vc, slots, total, row_vecs, num_slots, k_inv, v_inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_tokens_fp8(const int32_t* bt, int num_seqs, int max_blocks, const int32_t* pos,
+                                   const int32_t* qsl, int num_tokens, int block_size, const void* key,
+                                   const void* value, void* kc, void* vc, int row_elems, int64_t num_slots,
+                                   int64_t* slots, KvKind in_kind, float k_inv, float v_inv, hipStream_t stream) {
+  const int blocks = (num_tokens + kTokensPerWg - 1) / kTokensPerWg;
+  if (in_kind == KvKind::BF16)
+    hipLaunchKernelGGL(write_tokens_fp8_kernel<true>, dim3(blocks), dim3(256), 0, stream, bt, num_seqs, max_blocks,
+                       pos, qsl, num_tokens, block_size, key, value, (u32x4*)kc, (u32x4*)vc, row_elems / 16,
+                       num_slots, slots, k_inv, v_inv);
+  else
+    hipLaunchKernelGGL(write_tokens_fp8_kernel<false>, dim3(blocks), dim3(256), 0, stream, bt, num_seqs, max_blocks,
+                       pos, qsl, num_tokens, block_size, key, value, (u32x4*)kc, (u32x4*)vc, row_elems / 16,
+                       num_slots, slots, k_inv, v_inv);
+  return hipGetLastError();
 }
 
 hipError_t launch_write_tokens(const int32_t* bt, int num_seqs, int max_blocks, const int32_t* pos,

@@ -29,7 +29,10 @@
 //    16 B, four rows per instruction) and transposed inside each lane with
 //    v_perm_b32 into the A operand of the PV product.
 //  * bf16 uses v_mfma_f32_16x16x32_bf16 with P rounded to bf16; fp32 uses
-//    v_mfma_f32_16x16x4_f32 and keeps P in fp32.
+//    v_mfma_f32_16x16x4_f32 and keeps P in fp32.  FP8 (E4M3) pools are read
+//    at one byte per element, widened exactly to bf16 in registers and fed to
+//    the bf16 MFMA; k_scale is folded into the softmax scale and v_scale into
+//    the final normalisation.
 //  * Online softmax in the log2 domain: per chunk the max over tokens is
 //    reduced across the four 16-lane rows with two cross-lane xors; the sum
 //    stays lane-local until the end.  Masked tokens are excluded by select
@@ -65,7 +68,8 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, int s, int row,
   const Elem* vc = reinterpret_cast<const Elem*>(a.value_cache);
 
   typename Tile::Q q;
-  Tile::load_q(q, reinterpret_cast<const Elem*>(a.query) + ((int64_t)row * a.num_q_heads + hq0) * D, cols);
+  Tile::load_q(q, reinterpret_cast<const typename Tile::QElem*>(a.query) + ((int64_t)row * a.num_q_heads + hq0) * D,
+               cols);
 
   BlockWindow win;
   win.row = a.block_tables + (int64_t)s * a.max_blocks;
@@ -186,7 +190,7 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, int s, int row,
   lsum = wave_sum_across_rows(lsum);
   if (col >= cols) return;
   if (single) {
-    const float inv = 1.f / lsum;
+    const float inv = a.v_scale / lsum;
     float* dst = a.out + ((int64_t)row * a.num_q_heads + hq0 + col) * D;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -317,7 +321,7 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(const DecodeArgs a) 
       acc = acc * s_old + ok * s_new;
       M = mn;
     }
-    st16f(out + col * D + 4 * d4, acc * (1.f / Z));
+    st16f(out + col * D + 4 * d4, acc * (a.v_scale / Z));
   }
 }
 
@@ -357,11 +361,16 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream, hipEv
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int head_dim, int block_size, bool bf16,
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int block_size, KvKind kind,
                          hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
 #define PKV_CASE(T, D, BS) \
   if (head_dim == D && block_size == BS) return launch_decode_t<T<D, BS>>(a, stream, e0, e1);
-  if (bf16) {
+  if (kind == KvKind::FP8) {
+    PKV_CASE(TileFp8, 128, 16)
+    PKV_CASE(TileFp8, 128, 32)
+    PKV_CASE(TileFp8, 64, 16)
+    PKV_CASE(TileFp8, 64, 32)
+  } else if (kind == KvKind::BF16) {
     PKV_CASE(TileBf16, 128, 16)
     PKV_CASE(TileBf16, 128, 32)
     PKV_CASE(TileBf16, 64, 16)

@@ -7,6 +7,9 @@
 
 namespace pkv {
 
+// Element type of the KV pools (queries are bf16 for BF16 and FP8, fp32 for F32).
+enum class KvKind { F32, BF16, FP8 };
+
 // Everything the decode kernels read; built and validated by the API layer.
 struct DecodeArgs {
   float* out;                 // [B, Hq, D] (decode) or [T, Hq, D] (varlen rows)
@@ -27,7 +30,8 @@ struct DecodeArgs {
   int head_tiles;             // ceil(group / 16)
   int tile_cols;              // min(group, 16)
   int64_t num_blocks;
-  float scale_log2;           // scale * log2(e)
+  float scale_log2;           // scale * log2(e) (times k_scale for FP8 pools)
+  float v_scale;              // multiplies every output (FP8 pools; 1 otherwise)
   int workers;                // wavefronts sharing the work (split points)
   // workspace
   int* cum;                   // [B + 1] chunk prefix sums (written by the split kernel)
@@ -39,7 +43,7 @@ size_t decode_workspace_bytes(int num_seqs, int num_kv_heads, int group, int hea
 // Splits the workspace into the DecodeArgs pointers.
 void decode_workspace_carve(DecodeArgs& a, void* ws, int head_dim);
 
-hipError_t launch_decode(const DecodeArgs& a, int head_dim, int block_size, bool bf16,
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int block_size, KvKind kind,
                          hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 hipError_t launch_slot_mapping(const int32_t* bt, int num_seqs, int max_blocks, const int32_t* pos,
@@ -54,6 +58,17 @@ hipError_t launch_write_tokens(const int32_t* bt, int num_seqs, int max_blocks, 
                                const int32_t* qsl, int num_tokens, int block_size, const void* key,
                                const void* value, void* kc, void* vc, int row_bytes, int64_t num_slots,
                                int64_t* slots, hipStream_t stream);
+
+// Quantising variants: key/value rows of `in_kind` (BF16 or F32) are stored
+// as E4M3 bytes of x * k_inv (v_inv); row_elems = num_kv_heads * head_dim
+// (a multiple of 16).
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* kc, void* vc,
+                                        const int64_t* slots, int num_tokens, int row_elems, int64_t num_slots,
+                                        KvKind in_kind, float k_inv, float v_inv, hipStream_t stream);
+hipError_t launch_write_tokens_fp8(const int32_t* bt, int num_seqs, int max_blocks, const int32_t* pos,
+                                   const int32_t* qsl, int num_tokens, int block_size, const void* key,
+                                   const void* value, void* kc, void* vc, int row_elems, int64_t num_slots,
+                                   int64_t* slots, KvKind in_kind, float k_inv, float v_inv, hipStream_t stream);
 
 // Whole-block copies for every (src, dst) pair of mapping (int64 [pairs][2]);
 // src1/dst1 may be null (one pool).  Pairs with an id outside its pool are
@@ -82,6 +97,7 @@ struct PrefillArgs {
   int group;
   int64_t num_blocks;
   float scale_log2;
+  float v_scale;              // multiplies every output (FP8 pools; 1 otherwise)
   int waves;                  // wavefronts in the grid
   int* plan;                  // workspace: item plan + work counter (prefill_plan_bytes)
 };
@@ -91,7 +107,7 @@ size_t prefill_plan_bytes(int num_seqs);
 
 // Dispatches to the workgroup-shared kernel (bf16, head_dim 128; plan kernel
 // first) or the per-wave kernel (other shapes).
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool bf16, int cus,
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, KvKind kind, int cus,
                           hipStream_t stream);
 hipError_t launch_prefill_lds(const PrefillArgs& a, int block_size, int cus, hipStream_t stream);
 

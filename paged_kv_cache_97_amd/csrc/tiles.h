@@ -8,6 +8,8 @@
 // accumulator's values are already the P^T operand's k-slots.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace pkv {
@@ -29,6 +31,7 @@ struct TileBf16 {
   static constexpr int VW = D / 16;   // dims per lane of a V row (= O^T dim tiles)
   static constexpr int NDT = D / 16;
   typedef uint16_t Elem;
+  typedef uint16_t QElem;
   typedef typename U32Vec<VW / 2>::type VVec;
 
   struct Q { u32x4 q[KK]; };
@@ -134,6 +137,7 @@ struct TileF32 {
   static constexpr int NH = D / 64;   // 64-dim halves of a V row
   static constexpr int NDT = D / 16;
   typedef float Elem;
+  typedef float QElem;
 
   struct Q { f32x4 q[NQ]; };
   struct Buf { f32x4 k[2][NQ]; f32x4 v[2][4][NH]; };
@@ -216,6 +220,150 @@ struct TileF32 {
   static __device__ __forceinline__ int out_dim(int dt, int c, int r) {
     return 64 * (dt >> 2) + 16 * c + 4 * r + (dt & 3);
   }
+};
+
+// ------------------------------------------------------------------ fp8 tile
+// KV pools hold OCP E4M3 bytes, the query is bf16.  Every E4M3 value is
+// exactly a bf16 value, so tiles are widened in registers
+// (v_cvt_scalef32_pk_bf16_fp8, scale 1) and fed to the bf16 MFMA; the pool
+// scales are applied outside the tile (k_scale folded into the softmax scale,
+// v_scale into the final normalisation).
+//
+// QK contraction order: the dot product may visit dims in any order as long
+// as K and Q agree, so lane row-group c owns the contiguous dims
+// [c*D/4, (c+1)*D/4) of a K row (D/4 bytes: one or two 16-byte loads) and
+// k-step kk uses dims c*D/4 + 8kk .. +7 of both operands.
+// V keeps the bf16 tile's layout (rows 4c + r, dims VW*i ..), at one byte per
+// element, and is widened before the same in-lane transpose.
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                      : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int D_, int BS_>
+struct TileFp8 {
+  static constexpr int D = D_;
+  static constexpr int BS = BS_;
+  static constexpr bool kDoubleBuffer = true;
+  static constexpr int kWavesPerEU = 2;
+  static constexpr int KK = D / 32;   // bf16 MFMA k-steps of the QK contraction
+  static constexpr int KB = D / 4;    // K bytes per lane and row
+  static constexpr int KV = KB / 16;  // 16-byte K loads per lane and row
+  static constexpr int VW = D / 16;   // V dims (bytes) per lane and row
+  static constexpr int NDT = D / 16;
+  typedef uint8_t Elem;
+  typedef uint16_t QElem;
+  typedef typename U32Vec<VW / 2>::type VVec;                   // widened V piece (bf16)
+  typedef typename std::conditional<VW == 8, u32x2, uint32_t>::type VRaw;
+
+  struct Q { u32x4 q[KK]; };
+  struct Buf { u32x4 k[2][KV]; VRaw v[2][4]; };
+
+  static __device__ __forceinline__ void load_q(Q& q, const QElem* qb, int cols) {
+    const int l = lane_id(), i = l & 15, c = l >> 4;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      q.q[kk] = (i < cols) ? ld16(qb + i * D + KB * c + 8 * kk) : u32x4{0, 0, 0, 0};
+  }
+
+  static __device__ __forceinline__ void load_q_col(Q& q, const QElem* colp, bool valid) {
+    const int c = lane_id() >> 4;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) q.q[kk] = valid ? ld16(colp + KB * c + 8 * kk) : u32x4{0, 0, 0, 0};
+  }
+
+  static __device__ __forceinline__ int k_lane_off(int rs) {
+    const int l = lane_id();
+    return (l & 15) * rs + KB * (l >> 4);
+  }
+  static __device__ __forceinline__ int v_lane_off(int rs) {
+    const int l = lane_id();
+    return 4 * (l >> 4) * rs + VW * (l & 15);
+  }
+
+  template <bool STREAM = true>
+  static __device__ __forceinline__ void load(Buf& b, const Elem* const kp[2], const Elem* const vp[2],
+                                              int koff, int voff, int rs) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int j = 0; j < KV; ++j) b.k[u][j] = ld_v<u32x4, STREAM>(kp[u] + koff + 16 * j);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b.v[u][r] = ld_v<VRaw, STREAM>(vp[u] + voff + r * rs);
+    }
+  }
+
+  static __device__ __forceinline__ void qk(const Buf& b, const Q& q, f32x4 s[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        // 8 bytes = dims c*D/4 + 8kk .. +7 of this lane's K row
+        const uint32_t w0 = b.k[u][kk >> 1][2 * (kk & 1)];
+        const uint32_t w1 = b.k[u][kk >> 1][2 * (kk & 1) + 1];
+        const u32x4 a = {fp8x2_to_bf16x2(w0, false), fp8x2_to_bf16x2(w0, true), fp8x2_to_bf16x2(w1, false),
+                         fp8x2_to_bf16x2(w1, true)};
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, q.q[kk]), s[u], 0, 0, 0);
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void zero_v_rows(Buf& b, int valid) {
+    const int c = lane_id() >> 4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (16 * u + 4 * c + r >= valid) b.v[u][r] = VRaw{};
+  }
+
+  static __device__ __forceinline__ VVec widen(const VRaw& x) {
+    VVec y;
+    if constexpr (VW == 8) {
+      y[0] = fp8x2_to_bf16x2(x[0], false);
+      y[1] = fp8x2_to_bf16x2(x[0], true);
+      y[2] = fp8x2_to_bf16x2(x[1], false);
+      y[3] = fp8x2_to_bf16x2(x[1], true);
+    } else {
+      y[0] = fp8x2_to_bf16x2(x, false);
+      y[1] = fp8x2_to_bf16x2(x, true);
+    }
+    return y;
+  }
+
+  static __device__ __forceinline__ uint32_t pick(const VVec& a, const VVec& b, int t) {
+    const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+    return __builtin_amdgcn_perm(b[t >> 1], a[t >> 1], sel);
+  }
+
+  // Same k-slot order as the bf16 tile: slot 4u + r is token 16u + 4c + r.
+  static __device__ __forceinline__ void pv(const Buf& b, const float p[2][4], f32x4 o[NDT]) {
+    bf16x8 pb;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pb[4 * u + r] = (__bf16)p[u][r];
+    VVec w[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[u][r] = widen(b.v[u][r]);
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) {
+      u32x4 a;
+      a[0] = pick(w[0][0], w[0][1], t);
+      a[1] = pick(w[0][2], w[0][3], t);
+      a[2] = pick(w[1][0], w[1][1], t);
+      a[3] = pick(w[1][2], w[1][3], t);
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pb, o[t], 0, 0, 0);
+    }
+  }
+
+  static __device__ __forceinline__ int out_dim(int dt, int c, int r) { return VW * (4 * c + r) + dt; }
 };
 
 // ------------------------------------------------------------ block id window

@@ -43,7 +43,7 @@ prefill_kernel(const PrefillArgs a) {
   const int rs = Hkv * D;
   const Elem* kc = reinterpret_cast<const Elem*>(a.key_cache);
   const Elem* vc = reinterpret_cast<const Elem*>(a.value_cache);
-  const Elem* qbase = reinterpret_cast<const Elem*>(a.query);
+  const typename Tile::QElem* qbase = reinterpret_cast<const typename Tile::QElem*>(a.query);
   const int koff = Tile::k_lane_off(rs);
   const int voff = Tile::v_lane_off(rs);
 
@@ -205,7 +205,7 @@ prefill_kernel(const PrefillArgs a) {
       const int f = f0 + 16 * t + col;
       if (f >= f1) continue;
       const int row = f / G, head = f - row * G;
-      const float inv = 1.f / tot;
+      const float inv = a.v_scale / tot;
       float* dst = a.out + ((int64_t)(qrow0 + row) * Hq + h * G + head) * D;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -231,12 +231,17 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool bf16, int cus,
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, KvKind kind, int cus,
                           hipStream_t stream) {
-  if (bf16 && head_dim == 128) return launch_prefill_lds(a, block_size, cus, stream);
+  if (kind == KvKind::BF16 && head_dim == 128) return launch_prefill_lds(a, block_size, cus, stream);
 #define PKV_CASE(T, B, D, BS) \
   if (head_dim == D && block_size == BS) return launch_prefill_t<T<D, BS>, PrefillTiles<B, D>::value>(a, stream);
-  if (bf16) {
+  if (kind == KvKind::FP8) {
+    PKV_CASE(TileFp8, true, 128, 16)
+    PKV_CASE(TileFp8, true, 128, 32)
+    PKV_CASE(TileFp8, true, 64, 16)
+    PKV_CASE(TileFp8, true, 64, 32)
+  } else if (kind == KvKind::BF16) {
     PKV_CASE(TileBf16, true, 128, 16)
     PKV_CASE(TileBf16, true, 128, 32)
     PKV_CASE(TileBf16, true, 64, 16)

@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
-PKV_F32, PKV_BF16 = 0, 1
+PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 _c_i32, _c_i64, _c_f32, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
 _SIGNATURES = {
@@ -36,6 +36,16 @@ _SIGNATURES = {
     "pkv_paged_attention_varlen": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,
                                             _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
                                             _c_f32, _c_i32, _c_vp, _c_sz, _c_vp]),
+    "pkv_reshape_and_cache_fp8": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i64,
+                                           _c_i32, _c_i32, _c_f32, _c_f32, _c_vp]),
+    "pkv_write_new_tokens_fp8": (_c_i32, [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
+                                          _c_vp, _c_i32, _c_i32, _c_i64, _c_i32, _c_f32, _c_f32, _c_vp, _c_vp]),
+    "pkv_paged_attention_decode_fp8": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32, _c_i32,
+                                                _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_f32, _c_f32, _c_f32,
+                                                _c_vp, _c_sz, _c_vp]),
+    "pkv_paged_attention_varlen_fp8": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,
+                                                _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
+                                                _c_f32, _c_f32, _c_f32, _c_vp, _c_sz, _c_vp]),
     "pkv_copy_blocks": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp]),
     "pkv_swap_blocks": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_vp]),
     "pkv_set_profile_events": (_c_i32, [_c_vp, _c_vp]),
@@ -225,6 +235,113 @@ def paged_attention_varlen(query: torch.Tensor, key_cache: torch.Tensor, value_c
         _dev(query_start_loc, "query_start_loc", torch.int32, 1), B, T, int(max_query_len), int(max_seq_len),
         Hq, Hkv, D, NB, bs, float(scale), _kv_dtype(query), _dev(ws, "workspace"),
         ws.numel() * ws.element_size(), _stream(query)), "paged_attention_varlen")
+    return out
+
+
+# ----------------------------------------------------------------- FP8 (E4M3) pools
+_FP8_POOL = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _fp8_pools(key_cache: torch.Tensor, value_cache: torch.Tensor) -> None:
+    if key_cache.dtype not in _FP8_POOL or value_cache.dtype not in _FP8_POOL:
+        raise ValueError("E4M3 pools must be uint8 or float8_e4m3fn tensors")
+    if value_cache.shape != key_cache.shape:
+        raise ValueError("key_cache and value_cache shapes differ")
+
+
+def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                          value_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float,
+                          v_scale: float) -> None:
+    """reshape_and_cache into E4M3 pools: code = E4M3(x * (1/scale)), saturating."""
+    T, Hkv, D = key.shape
+    _fp8_pools(key_cache, value_cache)
+    NB, bs = key_cache.shape[0], key_cache.shape[1]
+    if value.shape != key.shape or key_cache.shape[2:] != (Hkv, D) or value.dtype != key.dtype:
+        raise ValueError("key/value/cache shapes disagree")
+    if slot_mapping.shape[0] != T:
+        raise ValueError("slot_mapping must have one entry per token")
+    _check(lib().pkv_reshape_and_cache_fp8(_dev(key, "key", ndim=3), _dev(value, "value", ndim=3),
+                                           _dev(key_cache, "key_cache", ndim=4),
+                                           _dev(value_cache, "value_cache", ndim=4),
+                                           _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, Hkv, D, NB, bs,
+                                           _kv_dtype(key), float(k_scale), float(v_scale), _stream(key)),
+           "reshape_and_cache_fp8")
+
+
+def write_new_tokens_fp8(block_tables: torch.Tensor, positions: torch.Tensor, query_start_loc: torch.Tensor,
+                         block_size: int, key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                         value_cache: torch.Tensor, k_scale: float, v_scale: float,
+                         slot_mapping: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """write_new_tokens into E4M3 pools (slot mapping + quantising write)."""
+    B, M = block_tables.shape
+    T, Hkv, D = key.shape
+    _fp8_pools(key_cache, value_cache)
+    NB, bs = key_cache.shape[0], key_cache.shape[1]
+    if value.shape != key.shape or key_cache.shape[2:] != (Hkv, D) or value.dtype != key.dtype:
+        raise ValueError("key/value/cache shapes disagree")
+    if positions.shape[0] != T or query_start_loc.shape[0] != B + 1 or bs != block_size:
+        raise ValueError("positions/query_start_loc/block_size do not match")
+    sp = _dev(slot_mapping, "slot_mapping", torch.int64, 1) if slot_mapping is not None else None
+    _check(lib().pkv_write_new_tokens_fp8(_dev(block_tables, "block_tables", torch.int32, 2), B, M,
+                                          _dev(positions, "positions", torch.int32, 1),
+                                          _dev(query_start_loc, "query_start_loc", torch.int32, 1), T,
+                                          int(block_size), _dev(key, "key", ndim=3), _dev(value, "value", ndim=3),
+                                          _dev(key_cache, "key_cache", ndim=4),
+                                          _dev(value_cache, "value_cache", ndim=4), Hkv, D, NB, _kv_dtype(key),
+                                          float(k_scale), float(v_scale), sp, _stream(key)), "write_new_tokens_fp8")
+    return slot_mapping
+
+
+def paged_attention_decode_fp8(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                               block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float, max_seq_len: int,
+                               k_scale: float, v_scale: float, out: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention over E4M3 pools (K = code * k_scale, V = code * v_scale); bf16 query."""
+    B, Hq, D = query.shape
+    _fp8_pools(key_cache, value_cache)
+    NB, bs, Hkv, Dk = key_cache.shape
+    if Dk != D or query.dtype != torch.bfloat16:
+        raise ValueError("query must be bfloat16 [B, Hq, D] matching the pools")
+    if block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_tables/seq_lens must have num_seqs rows")
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=query.device)
+    nbytes = int(lib().pkv_decode_workspace_size(B, Hq, Hkv, D, bs, PKV_FP8_E4M3))
+    ws = _workspace(nbytes, query.device, workspace)
+    _check(lib().pkv_paged_attention_decode_fp8(
+        _dev(out, "out", torch.float32, 3), _dev(query, "query", ndim=3), _dev(key_cache, "key_cache", ndim=4),
+        _dev(value_cache, "value_cache", ndim=4), _dev(block_tables, "block_tables", torch.int32, 2),
+        block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32, 1), B, Hq, Hkv, D, NB, bs,
+        int(max_seq_len), float(scale), float(k_scale), float(v_scale), _dev(ws, "workspace"),
+        ws.numel() * ws.element_size(), _stream(query)), "paged_attention_decode_fp8")
+    return out
+
+
+def paged_attention_varlen_fp8(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                               block_tables: torch.Tensor, seq_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                               scale: float, max_query_len: int, max_seq_len: int, k_scale: float, v_scale: float,
+                               out: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Varlen attention over E4M3 pools; bf16 query."""
+    T, Hq, D = query.shape
+    _fp8_pools(key_cache, value_cache)
+    NB, bs, Hkv, Dk = key_cache.shape
+    B = seq_lens.shape[0]
+    if Dk != D or query.dtype != torch.bfloat16:
+        raise ValueError("query must be bfloat16 [T, Hq, D] matching the pools")
+    if block_tables.shape[0] != B or query_start_loc.shape[0] != B + 1:
+        raise ValueError("block_tables/query_start_loc do not match seq_lens")
+    if out is None:
+        out = torch.empty(T, Hq, D, dtype=torch.float32, device=query.device)
+    nbytes = int(lib().pkv_varlen_workspace_size(B, T, Hq, Hkv, D, max_query_len, bs, PKV_FP8_E4M3))
+    ws = _workspace(nbytes, query.device, workspace)
+    _check(lib().pkv_paged_attention_varlen_fp8(
+        _dev(out, "out", torch.float32, 3), _dev(query, "query", ndim=3), _dev(key_cache, "key_cache", ndim=4),
+        _dev(value_cache, "value_cache", ndim=4), _dev(block_tables, "block_tables", torch.int32, 2),
+        block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32, 1),
+        _dev(query_start_loc, "query_start_loc", torch.int32, 1), B, T, int(max_query_len), int(max_seq_len),
+        Hq, Hkv, D, NB, bs, float(scale), float(k_scale), float(v_scale), _dev(ws, "workspace"),
+        ws.numel() * ws.element_size(), _stream(query)), "paged_attention_varlen_fp8")
     return out
 
 

@@ -106,3 +106,27 @@ def test_block_copy_validation():
                                ctypes.c_void_p(1024), 3, 4, 4, 4096, None) == 1   # one value pool only
     assert lib.pkv_swap_blocks(None, None, None, None, None, 3, 4, -4, 4096, None) == 1
     assert lib.pkv_last_error()
+
+
+def test_fp8_validation_runs_before_any_launch():
+    lib = ops.lib()
+    nul = [None] * 5
+    # reshape_and_cache_fp8: no tokens -> OK; bad scales / dtype / row size -> errors
+    assert lib.pkv_reshape_and_cache_fp8(*nul, 0, 8, 128, 10, 16, 1, 0.5, 0.5, None) == 0
+    assert lib.pkv_reshape_and_cache_fp8(*nul, 0, 8, 128, 10, 16, 1, 0.0, 0.5, None) == 1
+    assert lib.pkv_reshape_and_cache_fp8(*nul, 0, 8, 128, 10, 16, 1, 0.5, float("inf"), None) == 1
+    assert lib.pkv_reshape_and_cache_fp8(*nul, 0, 8, 128, 10, 16, 2, 0.5, 0.5, None) == 2
+    assert lib.pkv_reshape_and_cache_fp8(*nul, 0, 1, 8, 10, 16, 1, 0.5, 0.5, None) == 2
+    assert lib.pkv_reshape_and_cache_fp8(*nul, 3, 8, 128, 10, 16, 1, 0.5, 0.5, None) == 1
+    args = [None, 2, 4, None, None, 0, 16, None, None, None, None, 8, 128, 10, 1, 0.5, 0.5, None, None]
+    assert lib.pkv_write_new_tokens_fp8(*args) == 0
+    bad = list(args); bad[15] = -1.0
+    assert lib.pkv_write_new_tokens_fp8(*bad) == 1
+    # decode: E4M3 pools through the plain call are refused; the fp8 call checks its scales
+    assert _decode(lib, dtype=2) == 1
+    assert lib.pkv_decode_workspace_size(128, 64, 8, 128, 16, 2) == lib.pkv_decode_workspace_size(128, 64, 8, 128, 16, 1)
+    a = [ctypes.c_void_p(1 << 20)] * 5
+    st = lib.pkv_paged_attention_decode_fp8(a[0], a[1], a[2], a[3], a[4], 4, ctypes.c_void_p(1 << 20), 2, 8, 2, 128,
+                                            10, 16, 64, 0.1, float("nan"), 1.0, ctypes.c_void_p(1 << 20), 1 << 30,
+                                            None)
+    assert st == 1 and b"scale" in lib.pkv_last_error()
