@@ -36,12 +36,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+W_BF16_NAN = np.uint16(0x7FC0)                # the workloads' free-slot poison (bf16 NaN)
 MFMA_BF16_TFLOPS = 2500.0
 METRIC = "paged-attn decode KV GB/s (% of MI355X HBM peak); seq-tokens/s per step"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_97_amd/csrc/decode_kernels.hip", "paged_kv_cache_97_amd/csrc/common.h",
                   "paged_kv_cache_97_amd/csrc/tiles.h", "paged_kv_cache_97_amd/csrc/launch.h"]
 CALIB_BYTES = 256 << 20
+FP8_K_SCALE, FP8_V_SCALE = 0.0125, 0.02      # per-pool scales of the E4M3 runs
 
 
 def kernel_source_hash() -> str:
@@ -120,10 +122,25 @@ def prefill_flops(wl) -> int:
     return total
 
 
-def _cpu_baseline(wl, budget_s: float = 12.0):
+def _fp8_sample(oracle, wl, kc, vc, s, scales):
+    """E4M3 pools holding only sequence s's blocks (free slots zeroed before
+    quantising) and its table renumbered into them."""
+    bs = wl.spec.block_size
+    nblk = -(-int(wl.seq_lens[s]) // bs)
+    ids = [int(b) for b in wl.block_tables[s, :nblk]]
+    nan = W_BF16_NAN
+    kb = np.where(kc[ids] == nan, 0, kc[ids]).astype(np.uint16)
+    vb = np.where(vc[ids] == nan, 0, vc[ids]).astype(np.uint16)
+    table = np.full((1, wl.block_tables.shape[1]), -1, np.int32)
+    table[0, :nblk] = np.arange(nblk)
+    return oracle.quantize_kv(kb, "bf16", scales[0]), oracle.quantize_kv(vb, "bf16", scales[1]), table
+
+
+def _cpu_baseline(wl, budget_s: float = 12.0, fp8_scales=None):
     """Time the oracle's attention on the batch's sequences, one at a time in
     batch order, until about budget_s of work is done; report the KV GB/s of
-    that sample (the same bytes model as the GPU value)."""
+    that sample (the same bytes model as the GPU value).  With fp8_scales the
+    oracle reads E4M3 pools (quantised per sequence outside the timed part)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -133,26 +150,30 @@ def _cpu_baseline(wl, budget_s: float = 12.0):
     slots = oracle.slot_mapping(wl.block_tables, wl.positions, wl.query_start_loc, wl.spec.block_size)
     kc, vc = oracle.reshape_and_cache(wl.key, wl.value, wl.key_cache, wl.value_cache, slots)
     decode = not wl.is_prefill.any()
-    t0 = time.perf_counter()
+    dt = 0.0
     done, tokens, rows = 0, 0, 0
-    while done < wl.num_seqs and time.perf_counter() - t0 < budget_s:
+    while done < wl.num_seqs and dt < budget_s:
         s = slice(done, done + 1)
         r0, r1 = int(wl.query_start_loc[done]), int(wl.query_start_loc[done + 1])
+        pk, pv, table, dts = kc, vc, wl.block_tables[s], wl.spec.dtype
+        if fp8_scales is not None:
+            pk, pv, table = _fp8_sample(oracle, wl, kc, vc, done, fp8_scales)
+        t0 = time.perf_counter()
         if decode:
-            oracle.decode_attention(wl.query[r0:r1], kc, vc, wl.block_tables[s], wl.seq_lens[s], wl.scale,
-                                    wl.spec.dtype)
+            oracle.decode_attention(wl.query[r0:r1], pk, pv, table, wl.seq_lens[s], wl.scale, dts, fp8_scales)
         else:
-            oracle.varlen_attention(wl.query[r0:r1], kc, vc, wl.block_tables[s], wl.seq_lens[s],
-                                    np.array([0, r1 - r0]), wl.scale, wl.spec.dtype)
+            oracle.varlen_attention(wl.query[r0:r1], pk, pv, table, wl.seq_lens[s], np.array([0, r1 - r0]),
+                                    wl.scale, dts, fp8_scales)
+        dt += time.perf_counter() - t0
         tokens += int(wl.seq_lens[done])
         rows += r1 - r0
         done += 1
-    dt = time.perf_counter() - t0
     sp = wl.spec
-    nbytes = tokens * 2 * sp.num_kv_heads * sp.head_dim * wl.elem_bytes
+    nbytes = tokens * 2 * sp.num_kv_heads * sp.head_dim * (1 if fp8_scales is not None else wl.elem_bytes)
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": "float64 NumPy oracle %s attention over the first %d of %d sequences "
-                      "(%d query rows, %d KV tokens), %.1f s" % ("decode" if decode else "varlen", done,
+            "sample": "float64 NumPy oracle %s%s attention over the first %d of %d sequences "
+                      "(%d query rows, %d KV tokens), %.1f s" % ("E4M3 " if fp8_scales else "",
+                                                                "decode" if decode else "varlen", done,
                                                                 wl.num_seqs, rows, tokens, dt),
             "seq_tokens_per_s": round(rows / dt, 3)}
 
@@ -226,6 +247,8 @@ def main() -> int:
     ap.add_argument("--summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of --kernels-only into %s" % os.path.relpath(TRAFFIC_FILE, ROOT))
     ap.add_argument("--command", default="", help="command line recorded with --summarize")
+    ap.add_argument("--kv-cache-dtype", choices=["auto", "fp8"], default="auto",
+                    help="auto: pools in the workload's dtype; fp8: OCP E4M3 pools (k/v scales %g/%g)" % (0.0125, 0.02))
     ap.add_argument("--blocks", action="store_true",
                     help="time the copy-on-write block copy and the GPU <-> pinned host swap instead")
     args = ap.parse_args()
@@ -263,6 +286,23 @@ def main() -> int:
 
     q, key, value = up(wl.query), up(wl.key), up(wl.value)
     kc, vc = up(wl.key_cache), up(wl.value_cache)
+    fp8 = args.kv_cache_dtype == "fp8"
+    if fp8:
+        if sp.dtype != "bf16":
+            print("bench.py: --kv-cache-dtype fp8 needs a bf16 workload", file=sys.stderr)
+            return 2
+        # E4M3 pools, filled from the resident bf16 pools by the library's own
+        # quantising write (every slot; free slots hold garbage codes, as reused
+        # blocks would)
+        nb_slots = kc.shape[0] * kc.shape[1]
+        kc8 = torch.empty(kc.shape, dtype=torch.uint8, device=dev)
+        vc8 = torch.empty(vc.shape, dtype=torch.uint8, device=dev)
+        ops.reshape_and_cache_fp8(kc.view(nb_slots, sp.num_kv_heads, sp.head_dim),
+                                  vc.view(nb_slots, sp.num_kv_heads, sp.head_dim), kc8, vc8,
+                                  torch.arange(nb_slots, dtype=torch.int64, device=dev), FP8_K_SCALE, FP8_V_SCALE)
+        torch.cuda.synchronize()
+        del kc, vc
+        kc, vc = kc8, vc8
     bt, sl, pos, qsl = up(wl.block_tables), up(wl.seq_lens), up(wl.positions), up(wl.query_start_loc)
     slots = torch.empty(wl.num_tokens, dtype=torch.int64, device=dev)
     out = torch.empty(wl.num_tokens, sp.num_q_heads, sp.head_dim, dtype=torch.float32, device=dev)
@@ -273,6 +313,16 @@ def main() -> int:
     torch.cuda.synchronize()
 
     def step():
+        if fp8:
+            ops.write_new_tokens_fp8(bt, pos, qsl, sp.block_size, key, value, kc, vc, FP8_K_SCALE, FP8_V_SCALE,
+                                     slots)
+            if varlen:
+                ops.paged_attention_varlen_fp8(q, kc, vc, bt, sl, qsl, wl.scale, wl.max_query_len, wl.max_seq_len,
+                                               FP8_K_SCALE, FP8_V_SCALE, out=out, workspace=ws)
+            else:
+                ops.paged_attention_decode_fp8(q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, FP8_K_SCALE, FP8_V_SCALE,
+                                               out=out, workspace=ws)
+            return
         # slot mapping + cache write of the step's new tokens (one fused kernel)
         ops.write_new_tokens(bt, pos, qsl, sp.block_size, key, value, kc, vc, slots)
         if varlen:
@@ -319,7 +369,7 @@ def main() -> int:
     torch.cuda.synchronize()
     kern_ms = [ops.HipEvent.elapsed_ms(e0, e1) for e0, e1 in evs]
     ms_step = total_ms / args.steps
-    kv_bytes = wl.kv_bytes_logical()
+    kv_bytes = wl.kv_bytes_logical() // (2 if fp8 else 1)
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     k_mean = float(np.mean(kern_ms))
     kname = "prefill_kernel" if varlen else "decode_split_kernel"
@@ -335,7 +385,7 @@ def main() -> int:
                 "flops_per_launch": flops}
     else:
         achieved = kv_bytes / (k_mean * 1e-3) / 1e9
-        tr = _load_traffic() if args.config == 3 else None
+        tr = _load_traffic() if args.config == 3 and not fp8 else None
         roof = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": round(tr["traffic_bytes_per_launch"]) if tr else None,
@@ -343,17 +393,20 @@ def main() -> int:
                 "bytes_per_launch": kv_bytes}
     cpu = None
     if not args.no_cpu:
-        cpu = _cpu_baseline(wl)
+        cpu = _cpu_baseline(wl, fp8_scales=(FP8_K_SCALE, FP8_V_SCALE) if fp8 else None)
 
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if sp.dtype == "bf16" else "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "fp8-e4m3 KV, bf16 Q" if fp8 else ("bf16" if sp.dtype == "bf16" else "f32"),
+        "data": "synthetic",
         "config": {"workload": sp.name, "num_seqs": wl.num_seqs, "num_q_heads": sp.num_q_heads,
                    "num_kv_heads": sp.num_kv_heads, "head_dim": sp.head_dim, "block_size": sp.block_size,
                    "sum_seq_len": int(wl.seq_lens.sum()), "max_seq_len": wl.max_seq_len, "seed": wl.seed,
-                   "step": "write_new_tokens (slot mapping + reshape_and_cache) + paged_attention_%s"
-                           % ("varlen" if varlen else "decode")},
+                   "kv_cache_dtype": "fp8 (E4M3, k/v scales %g/%g)" % (FP8_K_SCALE, FP8_V_SCALE) if fp8
+                   else sp.dtype,
+                   "step": "write_new_tokens%s (slot mapping + reshape_and_cache) + paged_attention_%s%s"
+                           % ("_fp8" if fp8 else "", "varlen" if varlen else "decode", "_fp8" if fp8 else "")},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "seq_tokens_per_s": round(wl.num_tokens / (ms_step * 1e-3), 1),
         "kv_tokens_per_s": round(float(wl.seq_lens.sum()) / (ms_step * 1e-3), 1),
