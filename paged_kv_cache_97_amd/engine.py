@@ -1,0 +1,134 @@
+"""One-GPU step driver: runs the scheduler's plans through the library.
+
+Each step (gaoleia.github.io "PagedAttention 和 Continuous Batching" §2.3-§2.6;
+5688vip.com "vLLM核心机制" §3.3): the scheduler picks the rows; the engine
+moves swapped blocks (pkv_swap_blocks), writes the rows' new K/V into the
+paged pools (pkv_write_new_tokens) and runs attention over them
+(pkv_paged_attention_decode when every row is a single token, else
+pkv_paged_attention_varlen).  There is no model: every request's query, key
+and value rows are seeded synthetic values that depend only on (seed,
+request, position), so a token recomputed after a preemption gets the same
+K/V.  All device work runs in the library's kernels.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import ops
+from . import workloads as W
+from .scheduler import Scheduler, SchedulerConfig, StepPlan
+
+
+@dataclass
+class StepOutput:
+    plan: StepPlan
+    out: Optional[torch.Tensor]          # float32 [num_tokens, Hq, D], rows in plan order
+    query_start_loc: Optional[np.ndarray]
+
+
+class Engine:
+    def __init__(self, config: SchedulerConfig, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 seed: int = 0, kv_cache_dtype: str = "bf16", k_scale: float = 0.0125, v_scale: float = 0.02,
+                 device="cuda:0", gpu_order=None):
+        if kv_cache_dtype not in ("bf16", "fp8"):
+            raise ValueError("kv_cache_dtype must be 'bf16' or 'fp8'")
+        self.cfg = config
+        self.sched = Scheduler(config, gpu_order)
+        self.Hq, self.Hkv, self.D = num_q_heads, num_kv_heads, head_dim
+        self.seed = seed
+        self.kv = kv_cache_dtype
+        self.k_scale, self.v_scale = k_scale, v_scale
+        self.scale = 1.0 / float(np.sqrt(head_dim))
+        self.dev = torch.device(device)
+        shape = (config.num_gpu_blocks, config.block_size, num_kv_heads, head_dim)
+        pool_dtype = torch.uint8 if kv_cache_dtype == "fp8" else torch.bfloat16
+        self.key_cache = torch.empty(shape, dtype=pool_dtype, device=self.dev)
+        self.value_cache = torch.empty(shape, dtype=pool_dtype, device=self.dev)
+        self.cpu_key = self.cpu_value = None
+        if config.num_cpu_blocks > 0:
+            cshape = (config.num_cpu_blocks,) + shape[1:]
+            self.cpu_key = torch.empty(cshape, dtype=pool_dtype, pin_memory=True)
+            self.cpu_value = torch.empty(cshape, dtype=pool_dtype, pin_memory=True)
+        self.data: Dict[int, Tuple[np.ndarray, np.ndarray, np.ndarray]] = {}
+        ops.lib()                                     # fail loudly without the library
+
+    def add_request(self, req_id: int, prompt_len: int, max_new_tokens: int) -> None:
+        self.sched.add_request(req_id, prompt_len, max_new_tokens)
+        self.data[req_id] = W.request_tokens(self.seed, req_id, prompt_len + max_new_tokens, self.Hq, self.Hkv,
+                                             self.D, "bf16")
+
+    def has_work(self) -> bool:
+        return self.sched.has_work()
+
+    # ------------------------------------------------------------------ one step
+    def step_inputs(self, plan: StepPlan):
+        """Host arrays of the plan's rows: block tables, positions,
+        query_start_loc, seq_lens and the q/k/v rows (bf16 bits)."""
+        rows = plan.rows
+        B = len(rows)
+        width = max(1, max(len(r.block_table) for r in rows))
+        bt = np.full((B, width), -1, np.int32)
+        qsl = np.zeros(B + 1, np.int32)
+        sl = np.zeros(B, np.int32)
+        pos, q, k, v = [], [], [], []
+        for i, r in enumerate(rows):
+            bt[i, :len(r.block_table)] = r.block_table
+            qsl[i + 1] = qsl[i] + r.num_tokens
+            sl[i] = r.start + r.num_tokens
+            p = np.arange(r.start, r.start + r.num_tokens, dtype=np.int32)
+            dq, dk, dv = self.data[r.req_id]
+            pos.append(p)
+            q.append(dq[p])
+            k.append(dk[p])
+            v.append(dv[p])
+        return bt, np.concatenate(pos), qsl, sl, np.concatenate(q), np.concatenate(k), np.concatenate(v)
+
+    def _swap(self, pairs, to_cpu: bool) -> None:
+        m = torch.tensor(pairs, dtype=torch.int64, device=self.dev)
+        if to_cpu:
+            ops.swap_blocks(self.key_cache, self.value_cache, self.cpu_key, self.cpu_value, m)
+        else:
+            ops.swap_blocks(self.cpu_key, self.cpu_value, self.key_cache, self.value_cache, m)
+
+    def step(self) -> StepOutput:
+        plan = self.sched.schedule()
+        if plan.swap_out:
+            self._swap(plan.swap_out, True)
+        if plan.swap_in:
+            self._swap(plan.swap_in, False)
+        if not plan.rows:
+            self.sched.complete(plan)
+            return StepOutput(plan, None, None)
+        bt, pos, qsl, sl, q, k, v = self.step_inputs(plan)
+
+        def dev(a, bf16=False):
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            return (t.view(torch.bfloat16) if bf16 else t).to(self.dev, non_blocking=False)
+
+        tbt, tpos, tqsl, tsl = dev(bt), dev(pos), dev(qsl), dev(sl)
+        tq, tk, tv = dev(q, True), dev(k, True), dev(v, True)
+        bs = self.cfg.block_size
+        max_q = int(np.diff(qsl).max())
+        max_len = int(sl.max())
+        if self.kv == "fp8":
+            ops.write_new_tokens_fp8(tbt, tpos, tqsl, bs, tk, tv, self.key_cache, self.value_cache, self.k_scale,
+                                     self.v_scale)
+            if max_q == 1:
+                out = ops.paged_attention_decode_fp8(tq, self.key_cache, self.value_cache, tbt, tsl, self.scale,
+                                                     max_len, self.k_scale, self.v_scale)
+            else:
+                out = ops.paged_attention_varlen_fp8(tq, self.key_cache, self.value_cache, tbt, tsl, tqsl, self.scale,
+                                                     max_q, max_len, self.k_scale, self.v_scale)
+        else:
+            ops.write_new_tokens(tbt, tpos, tqsl, bs, tk, tv, self.key_cache, self.value_cache)
+            if max_q == 1:
+                out = ops.paged_attention_decode(tq, self.key_cache, self.value_cache, tbt, tsl, self.scale, max_len)
+            else:
+                out = ops.paged_attention_varlen(tq, self.key_cache, self.value_cache, tbt, tsl, tqsl, self.scale,
+                                                 max_q, max_len)
+        self.sched.complete(plan)
+        return StepOutput(plan, out, qsl)

@@ -283,3 +283,34 @@ def generate(cfg, seed: Optional[int] = None, keep_logical: bool = False) -> Wor
 def reduced(cfg: int, **overrides) -> WorkloadSpec:
     """A smaller variant of a config (same structure), for fast parity runs."""
     return CONFIGS[cfg].with_(**overrides)
+
+
+# ---------------------------------------------------------------- request streams
+def request_tokens(seed: int, req_id: int, length: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                   dtype: str = "bf16"):
+    """Synthetic query/key/value rows of one request, positions 0..length-1:
+    a pure function of (seed, req_id), so a token recomputed after a
+    preemption gets the same values.  Returns (q [L, Hq, D], k, v [L, Hkv, D])."""
+    rng = np.random.default_rng([int(seed), int(req_id)])
+    q = _draw_values(rng, (length, num_q_heads, head_dim), dtype)
+    k = _draw_values(rng, (length, num_kv_heads, head_dim), dtype)
+    v = _draw_values(rng, (length, num_kv_heads, head_dim), dtype)
+    return q, k, v
+
+
+def request_mix(seed: int, n: int, prompt=("lognormal", 300.0, LOGNORMAL_SIGMA, 8, 2048),
+                new_tokens=("uniform", 8, 64), arrivals_per_step: float = 0.0):
+    """n requests as (req_id, prompt_len, max_new_tokens, arrival_step): prompt
+    lengths from `prompt`, generation lengths from `new_tokens`; arrivals
+    all at step 0, or Poisson with the given mean per step."""
+    rng = np.random.default_rng([int(seed), 7])
+    p = _draw_lengths(rng, prompt, n)
+    g = _draw_lengths(rng, new_tokens, n)
+    if arrivals_per_step > 0:
+        gaps = rng.poisson(1.0 / arrivals_per_step, n) if arrivals_per_step < 1 else np.zeros(n, np.int64)
+        arr = np.cumsum(gaps)
+        if arrivals_per_step >= 1:
+            arr = np.arange(n) // int(arrivals_per_step)
+    else:
+        arr = np.zeros(n, np.int64)
+    return [(i, int(p[i]), int(g[i]), int(arr[i])) for i in range(n)]

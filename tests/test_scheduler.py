@@ -1,0 +1,128 @@
+"""Host step driver: scheduler policy and multi-step runs checked with the
+oracle (CPU only)."""
+import numpy as np
+import pytest
+
+from paged_kv_cache_97_amd import workloads as W
+from paged_kv_cache_97_amd.scheduler import Scheduler, SchedulerConfig
+from serving_harness import OracleEngine, dense_rows
+
+
+def _run(sched, max_steps=2000):
+    plans = []
+    while sched.has_work() and len(plans) < max_steps:
+        p = sched.schedule()
+        plans.append(p)
+        sched.complete(p)
+    assert not sched.has_work(), "did not drain"
+    return plans
+
+
+def test_budgets_chunks_and_row_order():
+    cfg = SchedulerConfig(block_size=16, num_gpu_blocks=400, max_num_seqs=5, max_num_batched_tokens=300,
+                          max_prefill_chunk=128)
+    s = Scheduler(cfg)
+    for rid, p, g, _ in W.request_mix(1, 12, prompt=("uniform", 20, 700), new_tokens=("uniform", 1, 40)):
+        s.add_request(rid, p, g)
+    for plan in _run(s):
+        assert len(plan.rows) <= 5 and plan.num_tokens <= 300
+        assert all(r.num_tokens <= 128 for r in plan.rows)
+        flags = [r.is_prefill for r in plan.rows]
+        assert flags == sorted(flags), "decode rows come before prefill chunks"
+        assert len({r.req_id for r in plan.rows}) == len(plan.rows)
+    assert s.gpu.num_free() == 400
+    assert all(r.status == "finished" and r.num_computed == r.total_len for r in s.requests.values())
+
+
+def test_fcfs_admission_and_positions_are_contiguous():
+    cfg = SchedulerConfig(block_size=16, num_gpu_blocks=64, max_num_seqs=2, max_num_batched_tokens=64,
+                          max_prefill_chunk=32)
+    s = Scheduler(cfg)
+    for i in range(5):
+        s.add_request(i, 40, 3)
+    admitted, seen = [], {}
+    for plan in _run(s):
+        for r in plan.rows:
+            if r.start == 0:
+                admitted.append(r.req_id)
+            assert seen.get(r.req_id, 0) == r.start, "each step continues where the last one stopped"
+            seen[r.req_id] = r.start + r.num_tokens
+    assert admitted == sorted(admitted) == list(range(5))
+    assert all(seen[i] == 43 for i in range(5))
+
+
+def test_watermark_holds_back_admission():
+    cfg = SchedulerConfig(block_size=16, num_gpu_blocks=20, max_num_seqs=8, max_num_batched_tokens=4096,
+                          max_prefill_chunk=512, watermark=0.25)
+    s = Scheduler(cfg)
+    s.add_request(0, 200, 4)      # 13 blocks: admitted on an idle engine
+    s.add_request(1, 40, 4)       # 3 more blocks would leave 4 < 5 free: held back
+    plan = s.schedule()
+    assert [r.req_id for r in plan.rows] == [0]
+    s.complete(plan)
+    assert [r.req_id for r in s.waiting] == [1]
+
+
+def test_lifo_preemption_by_recompute_then_completion():
+    cfg = SchedulerConfig(block_size=16, num_gpu_blocks=24, max_num_seqs=8, max_num_batched_tokens=512,
+                          max_prefill_chunk=64, watermark=0.0)
+    s = Scheduler(cfg)
+    for i in range(4):
+        s.add_request(i, 90, 40)      # 9 blocks each at the end: not all fit
+    plans = _run(s)
+    pre = [rid for p in plans for rid in p.preempted_ids]
+    assert pre, "the pool was meant to run out"
+    # the oldest request is never the victim while a newer one runs
+    assert 0 not in pre
+    assert all(r.status == "finished" for r in s.requests.values())
+    assert s.gpu.num_free() == 24
+    # a recomputed request re-prefills everything it had computed
+    victim = s.requests[pre[0]]
+    assert victim.recompute_to > 0
+
+
+def test_swap_preemption_moves_blocks_and_returns_them():
+    cfg = SchedulerConfig(block_size=16, num_gpu_blocks=24, num_cpu_blocks=32, max_num_seqs=8,
+                          max_num_batched_tokens=512, max_prefill_chunk=64, watermark=0.0, preemption="swap")
+    s = Scheduler(cfg)
+    for i in range(4):
+        s.add_request(i, 90, 40)
+    plans = _run(s)
+    outs = sum(len(p.swap_out) for p in plans)
+    ins = sum(len(p.swap_in) for p in plans)
+    assert outs > 0 and outs == ins
+    assert s.gpu.num_free() == 24 and s.cpu.num_free() == 32
+    # swapped requests resume where they stopped (no recompute)
+    assert all(r.recompute_to == 0 for r in s.requests.values())
+
+
+def test_rejects_requests_that_can_never_fit():
+    s = Scheduler(SchedulerConfig(block_size=16, num_gpu_blocks=4))
+    with pytest.raises(ValueError):
+        s.add_request(0, 60, 10)
+    with pytest.raises(ValueError):
+        SchedulerConfig(preemption="swap", num_cpu_blocks=0)
+
+
+@pytest.mark.parametrize("mode,kv", [("recompute", "bf16"), ("swap", "bf16"), ("recompute", "fp8")])
+def test_multistep_oracle_run_matches_dense_attention_every_step(mode, kv):
+    """Every row of every step, executed with the oracle on the paged pools
+    (swaps, cache writes, varlen attention), equals attention over the
+    request's own token list: the scheduler's tables, positions and swaps are
+    consistent across preemptions."""
+    cfg = SchedulerConfig(block_size=16, num_gpu_blocks=28, num_cpu_blocks=40 if mode == "swap" else 0,
+                          max_num_seqs=6, max_num_batched_tokens=160, max_prefill_chunk=48, watermark=0.05,
+                          preemption=mode)
+    eng = OracleEngine(cfg, num_q_heads=4, num_kv_heads=2, head_dim=16, seed=5, kv_cache_dtype=kv,
+                       gpu_order=np.random.default_rng(3).permutation(28))
+    for rid, p, g, _ in W.request_mix(11, 7, prompt=("uniform", 10, 150), new_tokens=("uniform", 5, 60)):
+        eng.add_request(rid, p, g)
+    steps, preempted = 0, 0
+    while eng.has_work():
+        plan, out = eng.step()
+        steps += 1
+        preempted += len(plan.preempted_ids)
+        if plan.rows:
+            np.testing.assert_allclose(out, dense_rows(eng, plan), rtol=0, atol=1e-12)
+        assert steps < 1000
+    assert preempted > 0
