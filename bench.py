@@ -235,6 +235,60 @@ def bench_blocks(args) -> int:
     return 0
 
 
+def bench_serve(args) -> int:
+    """The step driver (scheduler + engine) on the decode workload's model
+    shape: 64/8 heads, head_dim 128, 16-token blocks, bf16 (or --kv-cache-dtype
+    fp8) pools; 512 requests with lognormal prompts (median 1500 tokens,
+    clipped to [16, 8192]) and 32-256 new tokens each, all queued at the start;
+    at most 128 running sequences, 2048 batched tokens per step, 512-token
+    prefill chunks, a pool of 16384 blocks (262144 tokens).  --warmup steps are
+    run untimed, then --steps steps are timed end to end (host scheduling,
+    uploads and kernels); one JSON line."""
+    import torch
+    from paged_kv_cache_97_amd import workloads as W
+    from paged_kv_cache_97_amd.engine import Engine
+    from paged_kv_cache_97_amd.scheduler import SchedulerConfig
+    fp8 = args.kv_cache_dtype == "fp8"
+    cfg = SchedulerConfig(block_size=16, num_gpu_blocks=16384, max_num_seqs=128, max_num_batched_tokens=2048,
+                          max_prefill_chunk=512, watermark=0.01)
+    eng = Engine(cfg, 64, 8, 128, seed=1, kv_cache_dtype="fp8" if fp8 else "bf16",
+                 k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
+    for rid, p, g, _ in W.request_mix(1, 512, prompt=("lognormal", 1500.0, W.LOGNORMAL_SIGMA, 16, 8192),
+                                      new_tokens=("uniform", 32, 256)):
+        eng.add_request(rid, p, g)
+    for _ in range(args.warmup):
+        eng.step()
+    torch.cuda.synchronize()
+    tok = dec = pre_rows = preempt = 0
+    host = 0.0
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        if not eng.has_work():
+            break
+        h0 = time.perf_counter()
+        o = eng.step()
+        host += time.perf_counter() - h0
+        tok += o.plan.num_tokens
+        dec += o.plan.num_decode
+        pre_rows += o.plan.num_prefill
+        preempt += len(o.plan.preempted_ids)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rec = {
+        "metric": "step-driver throughput (tokens processed per second, prefill + decode)",
+        "value": round(tok / wall, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * wall / max(1, args.steps), 4), "higher_is_better": True,
+        "dtype": "fp8-e4m3 KV, bf16 Q" if fp8 else "bf16", "data": "synthetic",
+        "config": {"workload": "serve-512req-lognormal1500-new32to256-h64x8-d128",
+                   "max_num_seqs": 128, "max_num_batched_tokens": 2048, "prefill_chunk": 512,
+                   "pool_blocks": 16384},
+        "decode_tokens_per_s": round(dec / wall, 1), "prefill_rows": pre_rows, "preemptions": preempt,
+        "host_ms_per_step": round(1e3 * host / max(1, args.steps), 4),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,6 +303,8 @@ def main() -> int:
     ap.add_argument("--command", default="", help="command line recorded with --summarize")
     ap.add_argument("--kv-cache-dtype", choices=["auto", "fp8"], default="auto",
                     help="auto: pools in the workload's dtype; fp8: OCP E4M3 pools (k/v scales %g/%g)" % (0.0125, 0.02))
+    ap.add_argument("--serve", action="store_true",
+                    help="run the continuous-batching step driver over a synthetic request stream instead")
     ap.add_argument("--blocks", action="store_true",
                     help="time the copy-on-write block copy and the GPU <-> pinned host swap instead")
     args = ap.parse_args()
@@ -273,6 +329,8 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.blocks:
         return bench_blocks(args)
+    if args.serve:
+        return bench_serve(args)
     dev = torch.device("cuda:0")
     ops.lib()
     wl = W.generate(args.config)

@@ -7,13 +7,14 @@ paged pools (pkv_write_new_tokens) and runs attention over them
 (pkv_paged_attention_decode when every row is a single token, else
 pkv_paged_attention_varlen).  There is no model: every request's query, key
 and value rows are seeded synthetic values that depend only on (seed,
-request, position), so a token recomputed after a preemption gets the same
-K/V.  All device work runs in the library's kernels.
+request, position) -- a gather from a device-resident token bank -- so a
+token recomputed after a preemption gets the same K/V.  The path's work runs
+in the library's kernels.
 """
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import Dict, Optional, Tuple
+from typing import Optional
 
 import numpy as np
 import torch
@@ -53,39 +54,37 @@ class Engine:
             cshape = (config.num_cpu_blocks,) + shape[1:]
             self.cpu_key = torch.empty(cshape, dtype=pool_dtype, pin_memory=True)
             self.cpu_value = torch.empty(cshape, dtype=pool_dtype, pin_memory=True)
-        self.data: Dict[int, Tuple[np.ndarray, np.ndarray, np.ndarray]] = {}
+        self.bank = W.TokenBank(seed, 8192, num_q_heads, num_kv_heads, head_dim, "bf16")
+        self._bq, self._bk, self._bv = (torch.from_numpy(a).view(torch.bfloat16).to(self.dev)
+                                        for a in (self.bank.q, self.bank.k, self.bank.v))
         ops.lib()                                     # fail loudly without the library
 
     def add_request(self, req_id: int, prompt_len: int, max_new_tokens: int) -> None:
         self.sched.add_request(req_id, prompt_len, max_new_tokens)
-        self.data[req_id] = W.request_tokens(self.seed, req_id, prompt_len + max_new_tokens, self.Hq, self.Hkv,
-                                             self.D, "bf16")
 
     def has_work(self) -> bool:
         return self.sched.has_work()
 
     # ------------------------------------------------------------------ one step
     def step_inputs(self, plan: StepPlan):
-        """Host arrays of the plan's rows: block tables, positions,
-        query_start_loc, seq_lens and the q/k/v rows (bf16 bits)."""
+        """Host arrays of the plan's rows: block tables (padded with -1),
+        positions, query_start_loc, seq_lens and the token-bank rows."""
         rows = plan.rows
         B = len(rows)
         width = max(1, max(len(r.block_table) for r in rows))
         bt = np.full((B, width), -1, np.int32)
-        qsl = np.zeros(B + 1, np.int32)
-        sl = np.zeros(B, np.int32)
-        pos, q, k, v = [], [], [], []
         for i, r in enumerate(rows):
             bt[i, :len(r.block_table)] = r.block_table
-            qsl[i + 1] = qsl[i] + r.num_tokens
-            sl[i] = r.start + r.num_tokens
-            p = np.arange(r.start, r.start + r.num_tokens, dtype=np.int32)
-            dq, dk, dv = self.data[r.req_id]
-            pos.append(p)
-            q.append(dq[p])
-            k.append(dk[p])
-            v.append(dv[p])
-        return bt, np.concatenate(pos), qsl, sl, np.concatenate(q), np.concatenate(k), np.concatenate(v)
+        starts = np.fromiter((r.start for r in rows), np.int64, B)
+        counts = np.fromiter((r.num_tokens for r in rows), np.int64, B)
+        rids = np.fromiter((r.req_id for r in rows), np.int64, B)
+        qsl = np.zeros(B + 1, np.int32)
+        np.cumsum(counts, out=qsl[1:])
+        sl = (starts + counts).astype(np.int32)
+        T = int(qsl[-1])
+        pos = (np.arange(T) + np.repeat(starts - qsl[:-1], counts)).astype(np.int32)
+        idx = self.bank.index(np.repeat(rids, counts), pos)
+        return bt, pos, qsl, sl, idx
 
     def _swap(self, pairs, to_cpu: bool) -> None:
         m = torch.tensor(pairs, dtype=torch.int64, device=self.dev)
@@ -103,14 +102,17 @@ class Engine:
         if not plan.rows:
             self.sched.complete(plan)
             return StepOutput(plan, None, None)
-        bt, pos, qsl, sl, q, k, v = self.step_inputs(plan)
-
-        def dev(a, bf16=False):
-            t = torch.from_numpy(np.ascontiguousarray(a))
-            return (t.view(torch.bfloat16) if bf16 else t).to(self.dev, non_blocking=False)
-
-        tbt, tpos, tqsl, tsl = dev(bt), dev(pos), dev(qsl), dev(sl)
-        tq, tk, tv = dev(q, True), dev(k, True), dev(v, True)
+        bt, pos, qsl, sl, idx = self.step_inputs(plan)
+        # one pinned staging buffer and one asynchronous upload per step, so
+        # the host can plan the next step while this one runs
+        parts = (bt.reshape(-1), pos, qsl, sl, idx.astype(np.int32))
+        sizes = [a.size for a in parts]
+        stage = torch.empty(sum(sizes), dtype=torch.int32, pin_memory=True)
+        np.concatenate(parts, out=stage.numpy())
+        flat = stage.to(self.dev, non_blocking=True)
+        tbt, tpos, tqsl, tsl, tidx = torch.split(flat, sizes)
+        tbt = tbt.view(bt.shape)
+        tq, tk, tv = self._bq[tidx], self._bk[tidx], self._bv[tidx]
         bs = self.cfg.block_size
         max_q = int(np.diff(qsl).max())
         max_len = int(sl.max())

@@ -62,7 +62,7 @@ class SchedulerConfig:
             raise ValueError("sizes must be positive")
 
 
-@dataclass
+@dataclass(eq=False)                      # requests compare by identity
 class Request:
     """A request of prompt_len prompt tokens that generates max_new_tokens.
     Token positions 0 .. prompt_len + max_new_tokens - 1 are processed in
@@ -208,25 +208,29 @@ class Scheduler:
         # 2. running requests: decodes first, then prefill chunks, each in
         #    admission order; make room by preempting the newest running ones
         order = sorted(self.running, key=lambda r: (r.in_prefill, r.arrival))
+        running = set(map(id, self.running))
+        granted = set()
         for r in order:
-            if r not in self.running:
+            if id(r) not in running:
                 continue                                   # preempted while making room
             if budget_seqs == 0 or budget_tokens == 0:
                 break
             n = self._tokens_for(r, budget_tokens)
             need = self._blocks_needed(r, n)
             while self.gpu.num_free() < need:
-                victims = [v for v in self.running if v is not r and all(v is not g for g, _ in grants)]
+                victims = [v for v in self.running if v is not r and id(v) not in granted]
                 victim = max(victims, key=lambda v: v.arrival) if victims else None
                 if victim is None or victim.arrival < r.arrival:
                     victim = r                              # r itself is the newest: it yields
                 self._preempt(victim, plan)
+                running.discard(id(victim))
                 if victim is r:
                     break
-            if r not in self.running:
+            if id(r) not in running:
                 continue
             r.table.append_tokens(n, self.gpu)
             grants.append((r, n))
+            granted.add(id(r))
             budget_tokens -= n
             budget_seqs -= 1
 

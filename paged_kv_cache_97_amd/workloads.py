@@ -286,16 +286,29 @@ def reduced(cfg: int, **overrides) -> WorkloadSpec:
 
 
 # ---------------------------------------------------------------- request streams
-def request_tokens(seed: int, req_id: int, length: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                   dtype: str = "bf16"):
-    """Synthetic query/key/value rows of one request, positions 0..length-1:
-    a pure function of (seed, req_id), so a token recomputed after a
-    preemption gets the same values.  Returns (q [L, Hq, D], k, v [L, Hkv, D])."""
-    rng = np.random.default_rng([int(seed), int(req_id)])
-    q = _draw_values(rng, (length, num_q_heads, head_dim), dtype)
-    k = _draw_values(rng, (length, num_kv_heads, head_dim), dtype)
-    v = _draw_values(rng, (length, num_kv_heads, head_dim), dtype)
-    return q, k, v
+class TokenBank:
+    """Synthetic query/key/value rows for any (request, position): a bank of
+    `size` seeded rows, and token p of request r reads row
+    (r * 1000003 + p * 7919) mod size.  The values depend only on (seed, r,
+    p), so a token recomputed after a preemption gets the same K/V, and a
+    step's inputs are a gather from the bank (no per-token generation)."""
+
+    def __init__(self, seed: int, size: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 dtype: str = "bf16"):
+        rng = np.random.default_rng([int(seed), 99])
+        self.size = int(size)
+        self.q = _draw_values(rng, (self.size, num_q_heads, head_dim), dtype)
+        self.k = _draw_values(rng, (self.size, num_kv_heads, head_dim), dtype)
+        self.v = _draw_values(rng, (self.size, num_kv_heads, head_dim), dtype)
+
+    def index(self, req_id, positions) -> np.ndarray:
+        """Bank rows of tokens (req_id may be a scalar or one id per position)."""
+        p = np.asarray(positions, dtype=np.int64)
+        return (np.asarray(req_id, dtype=np.int64) * 1000003 + p * 7919) % self.size
+
+    def rows(self, req_id: int, positions):
+        i = self.index(req_id, positions)
+        return self.q[i], self.k[i], self.v[i]
 
 
 def request_mix(seed: int, n: int, prompt=("lognormal", 300.0, LOGNORMAL_SIGMA, 8, 2048),

@@ -31,12 +31,10 @@ class OracleEngine:
         cshape = (max(config.num_cpu_blocks, 1),) + shape[1:]
         self.ck = np.full(cshape, fill, dt)
         self.cv = np.full(cshape, fill, dt)
-        self.data = {}
+        self.bank = W.TokenBank(seed, 8192, num_q_heads, num_kv_heads, head_dim, "bf16")
 
     def add_request(self, req_id, prompt_len, max_new_tokens):
         self.sched.add_request(req_id, prompt_len, max_new_tokens)
-        self.data[req_id] = W.request_tokens(self.seed, req_id, prompt_len + max_new_tokens, self.Hq, self.Hkv,
-                                             self.D, "bf16")
 
     def has_work(self):
         return self.sched.has_work()
@@ -81,11 +79,11 @@ def step_inputs(eng, plan: StepPlan):
         qsl[i + 1] = qsl[i] + r.num_tokens
         sl[i] = r.start + r.num_tokens
         p = np.arange(r.start, r.start + r.num_tokens, dtype=np.int32)
-        dq, dk, dv = eng.data[r.req_id]
+        dq, dk, dv = eng.bank.rows(r.req_id, p)
         pos.append(p)
-        q.append(dq[p])
-        k.append(dk[p])
-        v.append(dv[p])
+        q.append(dq)
+        k.append(dk)
+        v.append(dv)
     return bt, np.concatenate(pos), qsl, sl, np.concatenate(q), np.concatenate(k), np.concatenate(v)
 
 
@@ -95,8 +93,8 @@ def dense_rows(eng, plan: StepPlan):
     G = eng.Hq // eng.Hkv
     outs = []
     for r in plan.rows:
-        dq, dk, dv = eng.data[r.req_id]
         L = r.start + r.num_tokens
+        dq, dk, dv = eng.bank.rows(r.req_id, np.arange(L))
         if eng.kv == "fp8":
             k = oracle.e4m3_value(oracle.quantize_kv(dk[:L], "bf16", eng.k_scale)) * eng.k_scale
             v = oracle.e4m3_value(oracle.quantize_kv(dv[:L], "bf16", eng.v_scale)) * eng.v_scale

@@ -126,3 +126,33 @@ def test_multistep_oracle_run_matches_dense_attention_every_step(mode, kv):
             np.testing.assert_allclose(out, dense_rows(eng, plan), rtol=0, atol=1e-12)
         assert steps < 1000
     assert preempted > 0
+
+
+def test_engine_step_inputs_equal_rowwise_construction():
+    """The engine's vectorised step inputs (tables, positions, offsets,
+    lengths, token-bank rows) equal the harness's row-by-row build."""
+    from paged_kv_cache_97_amd.engine import Engine
+    from serving_harness import step_inputs
+
+    class HostOnly:
+        pass
+
+    e = HostOnly()
+    e.bank = W.TokenBank(3, 8192, 4, 2, 16)
+    e.sched = Scheduler(SchedulerConfig(block_size=16, num_gpu_blocks=60, max_num_seqs=8,
+                                        max_num_batched_tokens=300, max_prefill_chunk=64, watermark=0.0))
+    for rid, p, g, _ in W.request_mix(2, 10, prompt=("uniform", 5, 200), new_tokens=("uniform", 1, 30)):
+        e.sched.add_request(rid, p, g)
+    n = 0
+    while e.sched.has_work():
+        plan = e.sched.schedule()
+        if plan.rows:
+            bt, pos, qsl, sl, idx = Engine.step_inputs(e, plan)
+            rb = step_inputs(e, plan)
+            for x, y in zip((bt, pos, qsl, sl), rb[:4]):
+                assert np.array_equal(x, y)
+            assert np.array_equal(e.bank.q[idx], rb[4]) and np.array_equal(e.bank.k[idx], rb[5])
+            assert np.array_equal(e.bank.v[idx], rb[6])
+            n += 1
+        e.sched.complete(plan)
+    assert n > 10
