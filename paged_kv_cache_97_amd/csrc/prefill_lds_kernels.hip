@@ -6,8 +6,12 @@
 //  * a workgroup of 8 waves (two per SIMD, so one wave's MFMAs overlap the
 //    other's softmax) owns an item of 256 (row, head) columns of one
 //    (sequence, KV head); each 32-token K/V chunk is loaded once per
-//    workgroup (coalesced 1 KB rows) into a double-buffered, XOR-swizzled LDS
-//    tile and read by all 8 waves, each computing 2 tiles of 16 columns;
+//    workgroup into double-buffered LDS and read by all 8 waves, each
+//    computing 2 tiles of 16 columns.  K is kept token-major (XOR-swizzled
+//    256 B rows); V is stored transposed (dim-major, 72 B rows of 32 tokens +
+//    pad) by a loader whose consecutive lanes hold consecutive tokens, so the
+//    transposed stores are contiguous and each lane reads its PV operand --
+//    8 tokens of one dim -- with two 8-byte reads, no in-register transpose;
 //  * the O^T accumulators stay in the accumulation registers: the softmax
 //    reference maximum is only moved when a column's maximum grows by more
 //    than 2^8 (the rescale is exact; weights up to 256 are fine in bf16/fp32),
@@ -117,7 +121,9 @@ __global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu
 prefill_lds_kernel(const PrefillArgs a) {
   typedef TileBf16<128, BS> Tile;
   constexpr int D = 128, NDT = 8, RB = 256;            // row bytes of one KV head
-  __shared__ __attribute__((aligned(16))) uint8_t kvbuf[2][2][32 * RB];   // [buffer][K|V][32 rows]
+  constexpr int VT = 72;                               // bytes per dim row of the transposed V tile
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][32 * RB];       // [buffer][32 token rows]
+  __shared__ __attribute__((aligned(16))) uint8_t vtbuf[2][D * VT];       // [buffer][128 dim rows]
   __shared__ int s_item;
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, col = l & 15, c = l >> 4;
   const int B = a.num_seqs, G = a.group, Hkv = a.num_kv_heads, Hq = a.num_q_heads;
@@ -130,7 +136,8 @@ prefill_lds_kernel(const PrefillArgs a) {
   const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.key_cache);
   const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.value_cache);
   const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.query);
-  const int ld_row = tid >> 4, ld_chunk = tid & 15;    // loader: 16 lanes per 256 B row (32 rows)
+  const int ld_row = tid >> 4, ld_chunk = tid & 15;    // K loader: 16 lanes per 256 B row (32 rows)
+  const int lv_row = tid & 31, lv_chunk = tid >> 5;    // V loader: 32 lanes per 16 B column
 
   while (true) {
     __syncthreads();                                   // everyone has read the previous item
@@ -181,20 +188,36 @@ prefill_lds_kernel(const PrefillArgs a) {
     // V (k = 1) chunk, bytes 16 * ld_chunk; rows past p_max load zeros.
     u32x4 R[2];
     auto load_chunk = [&](int ch) {
-      const int tok = ch * 32 + ld_row;
       const int lb0 = (ch * 32) / BS;                          // uniform
-      const int blk = BS == 16 ? (ld_row < 16 ? win.get(lb0) : win.get(lb0 + 1)) : win.get(lb0);
-      const int off = tok - (BS == 16 ? (lb0 + (ld_row >> 4)) : lb0) * BS;
+      const int b0 = win.get(lb0);
+      const int b1 = BS == 16 ? win.get(lb0 + 1) : b0;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        const uint16_t* base = (k == 0 ? kc : vc) + ((int64_t)blk * BS + off) * Hkv * D + h * D + 8 * ld_chunk;
+        const int r = k == 0 ? ld_row : lv_row, piece = k == 0 ? ld_chunk : lv_chunk;
+        const int tok = ch * 32 + r;
+        const int blk = BS == 16 && r >= 16 ? b1 : b0;
+        const int off = tok - (BS == 16 ? lb0 + (r >> 4) : lb0) * BS;
+        const uint16_t* base = (k == 0 ? kc : vc) + ((int64_t)blk * BS + off) * Hkv * D + h * D + 8 * piece;
         R[k] = tok <= p_max ? ld16(base) : u32x4{0, 0, 0, 0};
       }
     };
     auto store_chunk = [&](int b) {
+      *reinterpret_cast<u32x4*>(&kbuf[b][ld_row * RB + ((ld_chunk ^ (ld_row & 15)) << 4)]) = R[0];
+      // lanes 2m and 2m+1 hold tokens 2m, 2m+1: swap dwords with the partner
+      // (DPP quad_perm [1,0,3,2]) and write whole dwords (token pair, one dim):
+      // the even lane dims 2w, the odd lane dims 2w + 1
+      const bool odd = lv_row & 1;
+      const int tok2 = (lv_row & ~1) * 2;              // byte offset of the token pair
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
-        *reinterpret_cast<u32x4*>(&kvbuf[b][k][ld_row * RB + ((ld_chunk ^ (ld_row & 15)) << 4)]) = R[k];
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t mine = R[1][w];
+        const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)mine, 0xB1, 0xF, 0xF, true);
+        // even: (mine.lo, other.lo) = dim 2w of tokens (2m, 2m+1); odd: (other.hi, mine.hi) = dim 2w + 1
+        const uint32_t word = odd ? __builtin_amdgcn_perm(mine, other, 0x07060302u)
+                                  : __builtin_amdgcn_perm(other, mine, 0x05040100u);
+        const int dim = 8 * lv_chunk + 2 * w + (odd ? 1 : 0);
+        *reinterpret_cast<uint32_t*>(&vtbuf[b][dim * VT + tok2]) = word;
+      }
     };
 
     float mref[kPfTiles], lsum[kPfTiles];
@@ -213,7 +236,7 @@ prefill_lds_kernel(const PrefillArgs a) {
     float cmx[kPfTiles];
     auto scores = [&](int b, int ch, auto diag_tag) {
       constexpr bool DIAG = decltype(diag_tag)::value;
-      const uint8_t* Kt = kvbuf[b][0];
+      const uint8_t* Kt = kbuf[b];
       u32x4 kop[2][4];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -244,8 +267,10 @@ prefill_lds_kernel(const PrefillArgs a) {
       }
     };
     // Phase B: weights against the current reference maxima, then O^T += V^T P^T.
+    // Row i of O^T tile dt is dim i + 16 dt; k-slot 4u + r is token 16u + 4c + r,
+    // the order in which the S^T accumulator holds P.
     auto accumulate = [&](int b) {
-      const uint8_t* Vt = kvbuf[b][1];
+      const uint8_t* Vt = vtbuf[b];
       bf16x8 pb[kPfTiles];
 #pragma unroll
       for (int t = 0; t < kPfTiles; ++t) {
@@ -260,21 +285,12 @@ prefill_lds_kernel(const PrefillArgs a) {
           }
         lsum[t] += ps;
       }
-      u32x4 vr[2][4];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * u + 4 * c + r;
-          vr[u][r] = *reinterpret_cast<const u32x4*>(Vt + row * RB + ((col ^ (row & 15)) << 4));
-        }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        u32x4 av;
-        av[0] = Tile::pick(vr[0][0], vr[0][1], dt);
-        av[1] = Tile::pick(vr[0][2], vr[0][3], dt);
-        av[2] = Tile::pick(vr[1][0], vr[1][1], dt);
-        av[3] = Tile::pick(vr[1][2], vr[1][3], dt);
+        const uint8_t* vrow = Vt + (col + 16 * dt) * VT;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 8 * c);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 32 + 8 * c);
+        const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int t = 0; t < kPfTiles; ++t)
           o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb[t], o[t][dt], 0, 0, 0);
@@ -326,12 +342,9 @@ prefill_lds_kernel(const PrefillArgs a) {
       const float inv = 1.f / tot;
       float* dst = a.out + ((int64_t)(qrow0 + row) * Hq + h * G + head) * D;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int g = 0; g < NDT / 4; ++g)
-          st16f(dst + Tile::out_dim(4 * g, c, r),
-                f32x4{o[t][4 * g][r] * inv, o[t][4 * g + 1][r] * inv, o[t][4 * g + 2][r] * inv,
-                      o[t][4 * g + 3][r] * inv});
+      for (int dt = 0; dt < NDT; ++dt)             // rows 4c..4c+3 of tile dt: dims 16 dt + 4c ..
+        st16f(dst + 16 * dt + 4 * c,
+              f32x4{o[t][dt][0] * inv, o[t][dt][1] * inv, o[t][dt][2] * inv, o[t][dt][3] * inv});
     }
   }
 }
