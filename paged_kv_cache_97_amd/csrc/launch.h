@@ -105,11 +105,11 @@ struct PrefillArgs {
 // Workspace bytes of the prefill item plan for num_seqs sequences.
 size_t prefill_plan_bytes(int num_seqs);
 
-// Dispatches to the workgroup-shared kernel (bf16, head_dim 128; plan kernel
-// first) or the per-wave kernel (other shapes).
+// Dispatches to the workgroup-shared kernel (bf16 or FP8 pools, head_dim 128;
+// plan kernel first) or the per-wave kernel (other shapes).
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, KvKind kind, int cus,
                           hipStream_t stream);
-hipError_t launch_prefill_lds(const PrefillArgs& a, int block_size, int cus, hipStream_t stream);
+hipError_t launch_prefill_lds(const PrefillArgs& a, int block_size, bool fp8, int cus, hipStream_t stream);
 
 // Whole-block copies for every (src, dst) pair of mapping (int64 [pairs][2]);
 // src1/dst1 may be null (one pool).  Pairs with an id outside its pool are

@@ -116,7 +116,11 @@ prefill_plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__
   }
 }
 
-template <int BS>
+// FP8: the pools hold E4M3 bytes; the loader widens them exactly to bf16 on
+// their way into LDS (waves 0-3 load K, waves 4-7 V, 16 elements per lane), so
+// everything after the LDS tiles is the bf16 path.  k_scale is already in
+// scale_log2; v_scale multiplies the output.
+template <int BS, bool FP8>
 __global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_lds_kernel(const PrefillArgs a) {
   typedef TileBf16<128, BS> Tile;
@@ -133,8 +137,9 @@ prefill_lds_kernel(const PrefillArgs a) {
   const int* order = plan + kPlanHeader;
   const int* cum = order + B;
   int* counter = a.plan + 2;
-  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.key_cache);
-  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.value_cache);
+  typedef typename std::conditional<FP8, uint8_t, uint16_t>::type Elem;
+  const Elem* kc = reinterpret_cast<const Elem*>(a.key_cache);
+  const Elem* vc = reinterpret_cast<const Elem*>(a.value_cache);
   const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.query);
   const int ld_row = tid >> 4, ld_chunk = tid & 15;    // K loader: 16 lanes per 256 B row (32 rows)
   const int lv_row = tid & 31, lv_chunk = tid >> 5;    // V loader: 32 lanes per 16 B column
@@ -184,39 +189,68 @@ prefill_lds_kernel(const PrefillArgs a) {
     win.max_id = a.num_blocks - 1;
     win.fill(0);
 
-    // Loader: piece k of this thread is row ld_row (0..31) of the K (k = 0) or
-    // V (k = 1) chunk, bytes 16 * ld_chunk; rows past p_max load zeros.
+    // Loader (bf16): piece k of this thread is 16 bytes (8 dims) of row ld_row
+    // of the K chunk (k = 0) and of row lv_row of the V chunk (k = 1).  FP8:
+    // waves 0-3 load K (row tid >> 3, 16 dims), waves 4-7 V (row lane & 31,
+    // 16 dims).  Rows past p_max load zeros.
     u32x4 R[2];
+    const bool kthr = tid < kPfThreads / 2;            // FP8 only: this wave loads K
     auto load_chunk = [&](int ch) {
       const int lb0 = (ch * 32) / BS;                          // uniform
       const int b0 = win.get(lb0);
       const int b1 = BS == 16 ? win.get(lb0 + 1) : b0;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int r = k == 0 ? ld_row : lv_row, piece = k == 0 ? ld_chunk : lv_chunk;
+      auto fetch = [&](const Elem* pool, int r, int elem_off) {
         const int tok = ch * 32 + r;
         const int blk = BS == 16 && r >= 16 ? b1 : b0;
         const int off = tok - (BS == 16 ? lb0 + (r >> 4) : lb0) * BS;
-        const uint16_t* base = (k == 0 ? kc : vc) + ((int64_t)blk * BS + off) * Hkv * D + h * D + 8 * piece;
-        R[k] = tok <= p_max ? ld16(base) : u32x4{0, 0, 0, 0};
+        const Elem* base = pool + ((int64_t)blk * BS + off) * Hkv * D + h * D + elem_off;
+        return tok <= p_max ? ld16(base) : u32x4{0, 0, 0, 0};
+      };
+      if constexpr (FP8) {
+        R[0] = kthr ? fetch(kc, tid >> 3, 16 * (tid & 7)) : fetch(vc, lane_id() & 31, 16 * ((tid - kPfThreads / 2) >> 5));
+      } else {
+        R[0] = fetch(kc, ld_row, 8 * ld_chunk);
+        R[1] = fetch(vc, lv_row, 8 * lv_chunk);
       }
     };
-    auto store_chunk = [&](int b) {
-      *reinterpret_cast<u32x4*>(&kbuf[b][ld_row * RB + ((ld_chunk ^ (ld_row & 15)) << 4)]) = R[0];
-      // lanes 2m and 2m+1 hold tokens 2m, 2m+1: swap dwords with the partner
-      // (DPP quad_perm [1,0,3,2]) and write whole dwords (token pair, one dim):
-      // the even lane dims 2w, the odd lane dims 2w + 1
-      const bool odd = lv_row & 1;
-      const int tok2 = (lv_row & ~1) * 2;              // byte offset of the token pair
+    // V rows go in transposed: lanes 2m and 2m+1 hold tokens 2m, 2m+1; they
+    // swap dwords (DPP quad_perm [1,0,3,2]) and write whole dwords (token
+    // pair, one dim): the even lane dims 2w, the odd lane dims 2w + 1.
+    auto store_vt = [&](int b, int tok, int dim0, const uint32_t* d, auto nw_tag) {
+      constexpr int NW = decltype(nw_tag)::value;      // dwords (dim pairs) of this lane's token
+      const bool odd = tok & 1;
+      const int tok2 = (tok & ~1) * 2;                 // byte offset of the token pair
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t mine = R[1][w];
+      for (int w = 0; w < NW; ++w) {
+        const uint32_t mine = d[w];
         const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)mine, 0xB1, 0xF, 0xF, true);
         // even: (mine.lo, other.lo) = dim 2w of tokens (2m, 2m+1); odd: (other.hi, mine.hi) = dim 2w + 1
         const uint32_t word = odd ? __builtin_amdgcn_perm(mine, other, 0x07060302u)
                                   : __builtin_amdgcn_perm(other, mine, 0x05040100u);
-        const int dim = 8 * lv_chunk + 2 * w + (odd ? 1 : 0);
+        const int dim = dim0 + 2 * w + (odd ? 1 : 0);
         *reinterpret_cast<uint32_t*>(&vtbuf[b][dim * VT + tok2]) = word;
+      }
+    };
+    auto store_chunk = [&](int b) {
+      if constexpr (FP8) {
+        uint32_t d[8];                                 // 16 elements widened to bf16 pairs
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          d[2 * q4] = fp8x2_to_bf16x2(R[0][q4], false);
+          d[2 * q4 + 1] = fp8x2_to_bf16x2(R[0][q4], true);
+        }
+        if (kthr) {
+          const int row = tid >> 3, p = tid & 7;
+          *reinterpret_cast<u32x4*>(&kbuf[b][row * RB + (((2 * p) ^ (row & 15)) << 4)]) = u32x4{d[0], d[1], d[2], d[3]};
+          *reinterpret_cast<u32x4*>(&kbuf[b][row * RB + (((2 * p + 1) ^ (row & 15)) << 4)]) =
+              u32x4{d[4], d[5], d[6], d[7]};
+        } else {
+          store_vt(b, lane_id() & 31, 16 * ((tid - kPfThreads / 2) >> 5), d, std::integral_constant<int, 8>{});
+        }
+      } else {
+        *reinterpret_cast<u32x4*>(&kbuf[b][ld_row * RB + ((ld_chunk ^ (ld_row & 15)) << 4)]) = R[0];
+        const uint32_t d[4] = {R[1][0], R[1][1], R[1][2], R[1][3]};
+        store_vt(b, lv_row, 8 * lv_chunk, d, std::integral_constant<int, 4>{});
       }
     };
 
@@ -339,7 +373,7 @@ prefill_lds_kernel(const PrefillArgs a) {
       const int f = f0w + 16 * t + col;
       if (f >= f1w) continue;
       const int row = f / G, head = f - row * G;
-      const float inv = 1.f / tot;
+      const float inv = a.v_scale / tot;
       float* dst = a.out + ((int64_t)(qrow0 + row) * Hq + h * G + head) * D;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)             // rows 4c..4c+3 of tile dt: dims 16 dt + 4c ..
@@ -349,16 +383,20 @@ prefill_lds_kernel(const PrefillArgs a) {
   }
 }
 
-hipError_t launch_prefill_lds(const PrefillArgs& a, int block_size, int cus, hipStream_t stream) {
+hipError_t launch_prefill_lds(const PrefillArgs& a, int block_size, bool fp8, int cus, hipStream_t stream) {
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(256), 0, stream, a.qsl, a.seq_lens, a.num_seqs,
                      a.max_blocks * block_size, a.num_kv_heads, a.group, a.plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int grid = cus > 0 ? cus : 256;
-  if (block_size == 16)
-    hipLaunchKernelGGL(prefill_lds_kernel<16>, dim3(grid), dim3(kPfThreads), 0, stream, a);
+  if (block_size == 16 && !fp8)
+    hipLaunchKernelGGL((prefill_lds_kernel<16, false>), dim3(grid), dim3(kPfThreads), 0, stream, a);
+  else if (block_size == 16)
+    hipLaunchKernelGGL((prefill_lds_kernel<16, true>), dim3(grid), dim3(kPfThreads), 0, stream, a);
+  else if (!fp8)
+    hipLaunchKernelGGL((prefill_lds_kernel<32, false>), dim3(grid), dim3(kPfThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(prefill_lds_kernel<32>, dim3(grid), dim3(kPfThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_lds_kernel<32, true>), dim3(grid), dim3(kPfThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -233,7 +233,8 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, KvKind kind, int cus,
                           hipStream_t stream) {
-  if (kind == KvKind::BF16 && head_dim == 128) return launch_prefill_lds(a, block_size, cus, stream);
+  if ((kind == KvKind::BF16 || kind == KvKind::FP8) && head_dim == 128)
+    return launch_prefill_lds(a, block_size, kind == KvKind::FP8, cus, stream);
 #define PKV_CASE(T, B, D, BS) \
   if (head_dim == D && block_size == BS) return launch_prefill_t<T<D, BS>, PrefillTiles<B, D>::value>(a, stream);
   if (kind == KvKind::FP8) {
