@@ -305,6 +305,8 @@ def main() -> int:
                     help="auto: pools in the workload's dtype; fp8: OCP E4M3 pools (k/v scales %g/%g)" % (0.0125, 0.02))
     ap.add_argument("--serve", action="store_true",
                     help="run the continuous-batching step driver over a synthetic request stream instead")
+    ap.add_argument("--two-call", action="store_true",
+                    help="decode: time write_new_tokens + paged_attention_decode instead of the one-call decode_step")
     ap.add_argument("--blocks", action="store_true",
                     help="time the copy-on-write block copy and the GPU <-> pinned host swap instead")
     args = ap.parse_args()
@@ -370,7 +372,18 @@ def main() -> int:
                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
+    fused = not varlen and not args.two_call
+
     def step():
+        if fused:
+            # one call: the new tokens' slot mapping and cache write run inside
+            # the decode attention launch
+            if fp8:
+                ops.decode_step_fp8(q, key, value, kc, vc, bt, sl, wl.scale, wl.max_seq_len, FP8_K_SCALE,
+                                    FP8_V_SCALE, out=out, workspace=ws)
+            else:
+                ops.decode_step(q, key, value, kc, vc, bt, sl, wl.scale, wl.max_seq_len, out=out, workspace=ws)
+            return
         if fp8:
             ops.write_new_tokens_fp8(bt, pos, qsl, sp.block_size, key, value, kc, vc, FP8_K_SCALE, FP8_V_SCALE,
                                      slots)
@@ -463,8 +476,10 @@ def main() -> int:
                    "sum_seq_len": int(wl.seq_lens.sum()), "max_seq_len": wl.max_seq_len, "seed": wl.seed,
                    "kv_cache_dtype": "fp8 (E4M3, k/v scales %g/%g)" % (FP8_K_SCALE, FP8_V_SCALE) if fp8
                    else sp.dtype,
-                   "step": "write_new_tokens%s (slot mapping + reshape_and_cache) + paged_attention_%s%s"
-                           % ("_fp8" if fp8 else "", "varlen" if varlen else "decode", "_fp8" if fp8 else "")},
+                   "step": ("decode_step%s (slot mapping + reshape_and_cache fused into paged decode attention)"
+                            % ("_fp8" if fp8 else "")) if fused else
+                           ("write_new_tokens%s (slot mapping + reshape_and_cache) + paged_attention_%s%s"
+                            % ("_fp8" if fp8 else "", "varlen" if varlen else "decode", "_fp8" if fp8 else ""))},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "seq_tokens_per_s": round(wl.num_tokens / (ms_step * 1e-3), 1),
         "kv_tokens_per_s": round(float(wl.seq_lens.sum()) / (ms_step * 1e-3), 1),

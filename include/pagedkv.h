@@ -207,6 +207,44 @@ int pkv_paged_attention_decode_fp8(float* out, const void* query, const void* ke
                                    void* stream);
 
 /*
+ * One decode step in one call (gaoleia §2.4: the step first appends the new
+ * token's K and V to the sequence's last block, then attends over every
+ * token; §1.5 for the slot).  For each sequence s the new token is position
+ * seq_lens[s] - 1:
+ *   1. its rows key[s] and value[s] are written to its slot, exactly as
+ *      pkv_write_new_tokens with positions[s] = seq_lens[s] - 1 and
+ *      query_start_loc = 0, 1, ..., num_seqs would (no write when
+ *      seq_lens[s] == 0, when seq_lens[s] > max_blocks_per_seq * block_size,
+ *      or when the token's block id is outside [0, num_blocks));
+ *   2. out = pkv_paged_attention_decode over the pools as step 1 left them.
+ * Results equal those two calls bit for bit.  The write is fused into the
+ * attention launch: the wavefront that attends over the sequence's last
+ * chunk takes the new token's K/V from key/value and also stores them.
+ *   key, value   [num_seqs, num_kv_heads, head_dim] of dtype (device, read)
+ *   key_cache, value_cache  written at the new tokens' slots, read elsewhere
+ *   Other arguments, the workspace and the limits as for
+ *   pkv_paged_attention_decode (workspace from pkv_decode_workspace_size).
+ *   No sequence may read a slot that another sequence's new token writes
+ *   (such blocks must have been copied on write first).
+ */
+int pkv_decode_step(float* out, const void* query, const void* key, const void* value, void* key_cache,
+                    void* value_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
+                    pkv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_decode_step over E4M3 pools: query, key and value bfloat16; the write
+ * encodes as pkv_write_new_tokens_fp8 (in_dtype PKV_BF16) and the attention
+ * is pkv_paged_attention_decode_fp8, with the same k_scale / v_scale.
+ */
+int pkv_decode_step_fp8(float* out, const void* query, const void* key, const void* value, void* key_cache,
+                        void* value_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
+                        float k_scale, float v_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace pkv_paged_attention_varlen needs (current device).
  */
 size_t pkv_varlen_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,

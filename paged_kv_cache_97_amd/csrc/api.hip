@@ -327,7 +327,7 @@ static int run_decode(float* out, const void* query, const void* key_cache, cons
                       const int32_t* qsl, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t max_seq_len,
                       float scale, KvFormat fmt, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
+                      hipStream_t stream, const void* new_k = nullptr, const void* new_v = nullptr) {
   const int group = num_q_heads / num_kv_heads;
   const int workers = decode_workers();
   const int head_tiles = (group + 15) / 16;
@@ -357,6 +357,10 @@ static int run_decode(float* out, const void* query, const void* key_cache, cons
   a.scale_log2 = scale * fmt.k_scale * 1.4426950408889634f;
   a.v_scale = fmt.v_scale;
   a.workers = workers;
+  a.new_k = new_k;
+  a.new_v = new_v;
+  a.k_inv = fmt.kind == pkv::KvKind::FP8 ? 1.0f / fmt.k_scale : 1.0f;
+  a.v_inv = fmt.kind == pkv::KvKind::FP8 ? 1.0f / fmt.v_scale : 1.0f;
   pkv::decode_workspace_carve(a, workspace, head_dim);
   (void)max_seq_len;
   hipError_t e = pkv::launch_decode(a, head_dim, block_size, fmt.kind, stream, g_ev_start, g_ev_stop);
@@ -367,7 +371,8 @@ static int decode_impl(float* out, const void* query, const void* key_cache, con
                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale, pkv_dtype dtype,
-                       KvFormat fmt, void* workspace, size_t workspace_bytes, void* stream) {
+                       KvFormat fmt, void* workspace, size_t workspace_bytes, void* stream,
+                       const void* new_k = nullptr, const void* new_v = nullptr) {
   int st = check_shape(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || num_seqs > kMaxSeqs) return fail(PKV_EUNSUPPORTED, "num_seqs %d (max %d)", num_seqs, kMaxSeqs);
@@ -382,7 +387,7 @@ static int decode_impl(float* out, const void* query, const void* key_cache, con
   if (max_blocks_per_seq > 0 && num_blocks == 0) return fail(PKV_EINVAL, "empty pool with a non-empty block table");
   return run_decode(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens, nullptr,
                     num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_seq_len,
-                    scale, fmt, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+                    scale, fmt, workspace, workspace_bytes, static_cast<hipStream_t>(stream), new_k, new_v);
 }
 
 int pkv_paged_attention_decode(float* out, const void* query, const void* key_cache,
@@ -410,6 +415,34 @@ int pkv_paged_attention_decode_fp8(float* out, const void* query, const void* ke
                      num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_seq_len, scale,
                      PKV_FP8_E4M3, KvFormat{pkv::KvKind::FP8, k_scale, v_scale}, workspace, workspace_bytes,
                      stream);
+}
+
+int pkv_decode_step(float* out, const void* query, const void* key, const void* value, void* key_cache,
+                    void* value_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
+                    pkv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype == PKV_FP8_E4M3) return fail(PKV_EINVAL, "E4M3 pools need their scales: use pkv_decode_step_fp8");
+  if (num_seqs > 0 && (!key || !value)) return fail(PKV_EINVAL, "null pointer");
+  if (!aligned16(key) || !aligned16(value)) return fail(PKV_EINVAL, "key/value must be 16-byte aligned");
+  return decode_impl(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_seq_len, scale, dtype,
+                     plain_format(dtype), workspace, workspace_bytes, stream, key, value);
+}
+
+int pkv_decode_step_fp8(float* out, const void* query, const void* key, const void* value, void* key_cache,
+                        void* value_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
+                        float k_scale, float v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!good_scale(k_scale) || !good_scale(v_scale))
+    return fail(PKV_EINVAL, "k_scale %g / v_scale %g must be positive and finite", k_scale, v_scale);
+  if (num_seqs > 0 && (!key || !value)) return fail(PKV_EINVAL, "null pointer");
+  if (!aligned16(key) || !aligned16(value)) return fail(PKV_EINVAL, "key/value must be 16-byte aligned");
+  return decode_impl(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_seq_len, scale,
+                     PKV_FP8_E4M3, KvFormat{pkv::KvKind::FP8, k_scale, v_scale}, workspace, workspace_bytes,
+                     stream, key, value);
 }
 
 static size_t varlen_decode_part(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {

@@ -128,14 +128,6 @@ write_tokens_kernel(const int32_t* __restrict__ block_tables, int num_seqs, int 
 }
 
 // ------------------------------------------------------------------ FP8 stores
-// Four floats -> four E4M3 bytes (x * inv, saturated, round to nearest even).
-__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float inv) {
-  auto q = [inv](float x) { return fminf(fmaxf(x * inv, -448.f), 448.f); };
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q(a), q(b), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(q(c), q(d), w, true);
-  return (uint32_t)w;
-}
-
 // 16 E4M3 bytes from the 16 input elements of output vector `v` of a row
 // (bf16: two 16-byte input vectors, fp32: four).
 template <bool BF16IN>
@@ -148,8 +140,7 @@ __device__ __forceinline__ u32x4 quant16(const void* in, int64_t v, float inv) {
     for (int w = 0; w < 4; ++w) {
       const u32x4& x = w < 2 ? x0 : x1;
       const uint32_t lo = x[2 * (w & 1)], hi = x[2 * (w & 1) + 1];
-      out[w] = quant4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xFFFF0000u), __uint_as_float(hi << 16),
-                      __uint_as_float(hi & 0xFFFF0000u), inv);
+      out[w] = quant4(bf16_lo(lo), bf16_hi(lo), bf16_lo(hi), bf16_hi(hi), inv);
     }
   } else {
     const f32x4* p = reinterpret_cast<const f32x4*>(in) + 4 * v;

@@ -11,8 +11,19 @@ constexpr int kWave = 64;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// The lane index, recomputed where it is used.  A volatile asm is never
+// hoisted, so per-lane addresses built from it in rarely run code stay there
+// instead of becoming loop-invariant values that hold registers (or spill)
+// through a hot loop.
+__device__ __forceinline__ int lane_id_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 
 // Wave-uniform value into a scalar register.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -48,6 +59,26 @@ __device__ __forceinline__ float wave_sum_across_rows(float v) {
   v += __shfl_xor(v, 16);
   v += __shfl_xor(v, 32);
   return v;
+}
+
+// Four floats -> four OCP E4M3 bytes of x * inv (inv: the float32 reciprocal
+// of the pool scale), saturated to +-448, the largest finite E4M3 value, and
+// rounded to nearest even by v_cvt_pk_fp8_f32.  Byte k holds the k-th value.
+__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float inv) {
+  auto q = [inv](float x) { return fminf(fmaxf(x * inv, -448.f), 448.f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q(a), q(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(q(c), q(d), w, true);
+  return (uint32_t)w;
+}
+
+// bf16 element 0 / 1 of a dword as a float (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Eight bf16 values (element 2w in the low half of dword w) -> eight E4M3 bytes.
+__device__ __forceinline__ u32x2 quant8_bf16(const u32x4& x, float inv) {
+  return u32x2{quant4(bf16_lo(x[0]), bf16_hi(x[0]), bf16_lo(x[1]), bf16_hi(x[1]), inv),
+               quant4(bf16_lo(x[2]), bf16_hi(x[2]), bf16_lo(x[3]), bf16_hi(x[3]), inv)};
 }
 
 // Inclusive prefix sum over one wavefront.

@@ -53,9 +53,13 @@
 namespace pkv {
 
 // One range [c0, c1) of chunks of one pair.
+// tn >= 0: chunk c1 - 1 is the sequence's last and its token tn is the step's
+// new token (fused write); writer: this wave also stores it at element offset
+// new_row of the pools.
 template <class Tile>
 __device__ __forceinline__ void run_segment(const DecodeArgs& a, int s, int row, int h, int ht, int L,
-                                            int c0, int c1, bool single, int64_t slot) {
+                                            int c0, int c1, bool single, int64_t slot, int tn, bool writer,
+                                            int64_t new_row) {
   constexpr int D = Tile::D, BS = Tile::BS, NDT = Tile::NDT;
   typedef typename Tile::Elem Elem;
   const int l = lane_id(), col = l & 15, c = l >> 4;
@@ -137,8 +141,18 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, int s, int row,
     for (int t = 0; t < NDT; ++t) o[t] *= alpha;
     Tile::pv(b, p, o);
   };
-  // The last chunk of a range may be the sequence's partial chunk.
+  // The last chunk of a range may be the sequence's partial chunk, and may
+  // hold the step's new token: patched in from the input rows (the patch
+  // loads are issued only here, so the steady-state loop is unchanged) and
+  // stored to its slot by the writer.
   auto compute_last = [&](typename Tile::Buf& b, int ch) {
+    if (tn >= 0) {
+      const int64_t nrow = ((int64_t)s * Hkv + h) * D;
+      Tile::patch_new(b, tn, reinterpret_cast<const typename Tile::QElem*>(a.new_k) + nrow,
+                      reinterpret_cast<const typename Tile::QElem*>(a.new_v) + nrow, a.k_inv, a.v_inv);
+      if (writer)
+        Tile::store_new(b, tn, const_cast<Elem*>(kc) + new_row, const_cast<Elem*>(vc) + new_row);
+    }
     const int valid = uniform(L - ch * 32);
     if (valid < 32) compute(b, std::true_type{}, valid);
     else compute(b, std::false_type{}, 32);
@@ -256,10 +270,26 @@ decode_split_kernel(const DecodeArgs a) {
   int64_t remaining = x1 - x0;
   while (true) {
     const int seg = (int)min<int64_t>(n_s - ch, remaining);
-    const int L = uniform(clamp_len(a.seq_lens[s], max_tok));
+    const int raw_len = uniform(a.seq_lens[s]);
+    const int L = clamp_len(raw_len, max_tok);
     const int row = a.qsl ? uniform(a.qsl[s]) : s;
-    run_segment<Tile>(a, s, row, pr / a.head_tiles, pr % a.head_tiles, L, ch, ch + seg,
-                      ch == 0 && seg == n_s, (int64_t)s * ppseq + pr + w);
+    const int h = pr / a.head_tiles, ht = pr % a.head_tiles;
+    // Fused write: the range holding the sequence's last chunk owns the new
+    // token (position L - 1) when seq_lens was not clamped and the token's
+    // block id is in the pool (otherwise the slot is not written and the
+    // token is read from the pool, as a separate write would leave it).
+    int tn = -1;
+    int64_t new_row = 0;
+    if (a.new_k != nullptr && ch + seg == n_s && raw_len == L) {
+      const int lt = L - 1;
+      const int phys = uniform(a.block_tables[(int64_t)s * a.max_blocks + lt / Tile::BS]);
+      if (phys >= 0 && phys < a.num_blocks) {
+        tn = lt & 31;
+        new_row = (((int64_t)phys * Tile::BS + lt % Tile::BS) * a.num_kv_heads + h) * Tile::D;
+      }
+    }
+    run_segment<Tile>(a, s, row, h, ht, L, ch, ch + seg, ch == 0 && seg == n_s, (int64_t)s * ppseq + pr + w,
+                      tn, ht == 0, new_row);
     remaining -= seg;
     if (remaining <= 0) break;
     ch = 0;

@@ -33,6 +33,16 @@ struct DecodeArgs {
   float scale_log2;           // scale * log2(e) (times k_scale for FP8 pools)
   float v_scale;              // multiplies every output (FP8 pools; 1 otherwise)
   int workers;                // wavefronts sharing the work (split points)
+  // Optional fused cache write (decode only, qsl == NULL): new_k / new_v
+  // [B, Hkv, D] are the rows of each sequence's new token, position
+  // seq_lens[s] - 1 (query element type: float32 for F32 pools, bfloat16
+  // otherwise).  The token's slot is written and the attention takes the
+  // token's K/V from these rows.  k_inv / v_inv: float32 reciprocals of the
+  // pool scales (FP8 pools).
+  const void* new_k;
+  const void* new_v;
+  float k_inv;
+  float v_inv;
   // workspace
   int* cum;                   // [B + 1] chunk prefix sums (written by the split kernel)
   float* part_ml;             // [slots, tile_cols, 2]  (max, sum) in the log2 domain

@@ -14,8 +14,6 @@
 
 namespace pkv {
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 template <int N> struct U32Vec;
 template <> struct U32Vec<2> { typedef u32x2 type; };
 template <> struct U32Vec<4> { typedef u32x4 type; };
@@ -122,6 +120,49 @@ struct TileBf16 {
     }
   }
 
+  // ---- the step's new token (cache write fused into the attention launch)
+  // Token tn (0..31) of the loaded chunk is the step's new token, whose slot
+  // this launch writes: the lanes that hold its K and V rows replace them
+  // with this KV head's input rows nk / nv (pool element type).
+  static __device__ __forceinline__ void patch_new(Buf& b, int tn, const void* nkp, const void* nvp, float,
+                                                   float) {
+    const Elem* nk = static_cast<const Elem*>(nkp);
+    const Elem* nv = static_cast<const Elem*>(nvp);
+    const int l = lane_id_here(), i = l & 15, c = l >> 4;
+    const int t = tn & 15;
+    if (i == t)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const u32x4 x = ld16(nk + 8 * c + 32 * kk);
+        if (tn >= 16) b.k[1][kk] = x; else b.k[0][kk] = x;
+      }
+    if (c == (t >> 2)) {
+      const VVec x = *reinterpret_cast<const VVec*>(nv + VW * i);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * u + 4 * c + r == tn) b.v[u][r] = x;
+    }
+  }
+  // The lanes holding token tn's rows store them at kd / vd (its slot).
+  static __device__ __forceinline__ void store_new(const Buf& b, int tn, Elem* kd, Elem* vd) {
+    const int l = lane_id_here(), i = l & 15, c = l >> 4;
+    const int t = tn & 15;
+    if (i == t)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) st16(kd + 8 * c + 32 * kk, tn >= 16 ? b.k[1][kk] : b.k[0][kk]);
+    if (c == (t >> 2)) {
+      VVec x = b.v[0][0];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * u + 4 * c + r == tn) x = b.v[u][r];
+      *reinterpret_cast<VVec*>(vd + VW * i) = x;
+    }
+  }
+
   // Output dim held in o[dt][r] by a lane of row group c.
   static __device__ __forceinline__ int out_dim(int dt, int c, int r) { return VW * (4 * c + r) + dt; }
 };
@@ -215,6 +256,51 @@ struct TileF32 {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             o[4 * hf + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(b.v[u][r][hf][e], p[u][r], o[4 * hf + e], 0, 0, 0);
+  }
+
+  // ---- the step's new token: as TileBf16 (rows of float32).
+  static __device__ __forceinline__ void patch_new(Buf& b, int tn, const void* nkp, const void* nvp, float,
+                                                   float) {
+    const Elem* nk = static_cast<const Elem*>(nkp);
+    const Elem* nv = static_cast<const Elem*>(nvp);
+    const int l = lane_id_here(), i = l & 15, c = l >> 4;
+    const int t = tn & 15;
+    if (i == t)
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(nk + 16 * j + 4 * c);
+        if (tn >= 16) b.k[1][j] = x; else b.k[0][j] = x;
+      }
+    if (c == (t >> 2)) {
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(nv + 4 * i + 64 * hf);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * u + 4 * c + r == tn) b.v[u][r][hf] = x;
+      }
+    }
+  }
+  static __device__ __forceinline__ void store_new(const Buf& b, int tn, Elem* kd, Elem* vd) {
+    const int l = lane_id_here(), i = l & 15, c = l >> 4;
+    const int t = tn & 15;
+    if (i == t)
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) st16f(kd + 16 * j + 4 * c, tn >= 16 ? b.k[1][j] : b.k[0][j]);
+    if (c == (t >> 2)) {
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf) {
+        f32x4 x = b.v[0][0][hf];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * u + 4 * c + r == tn) x = b.v[u][r][hf];
+        st16f(vd + 4 * i + 64 * hf, x);
+      }
+    }
   }
 
   static __device__ __forceinline__ int out_dim(int dt, int c, int r) {
@@ -360,6 +446,54 @@ struct TileFp8 {
       a[2] = pick(w[1][0], w[1][1], t);
       a[3] = pick(w[1][2], w[1][3], t);
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pb, o[t], 0, 0, 0);
+    }
+  }
+
+  // ---- the step's new token.  Its input rows nk / nv are bfloat16 and the
+  // pool holds E4M3 codes: the lanes that hold token tn encode their pieces
+  // of the input rows exactly as the quantising cache write does
+  // (x * (1/scale), saturated, nearest even) and replace the loaded codes.
+  static __device__ __forceinline__ void patch_new(Buf& b, int tn, const void* nkp, const void* nvp, float k_inv,
+                                                   float v_inv) {
+    const uint16_t* nk = static_cast<const uint16_t*>(nkp);
+    const uint16_t* nv = static_cast<const uint16_t*>(nvp);
+    const int l = lane_id_here(), i = l & 15, c = l >> 4;
+    const int t = tn & 15;
+    if (i == t)
+#pragma unroll
+      for (int j = 0; j < KV; ++j) {
+        const u32x2 lo = quant8_bf16(ld16(nk + KB * c + 16 * j), k_inv);
+        const u32x2 hi = quant8_bf16(ld16(nk + KB * c + 16 * j + 8), k_inv);
+        const u32x4 code = {lo[0], lo[1], hi[0], hi[1]};
+        if (tn >= 16) b.k[1][j] = code; else b.k[0][j] = code;
+      }
+    if (c == (t >> 2)) {
+      const VVec x = *reinterpret_cast<const VVec*>(nv + VW * i);
+      VRaw vq;
+      if constexpr (VW == 8) vq = quant8_bf16(x, v_inv);
+      else vq = quant4(bf16_lo(x[0]), bf16_hi(x[0]), bf16_lo(x[1]), bf16_hi(x[1]), v_inv);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * u + 4 * c + r == tn) b.v[u][r] = vq;
+    }
+  }
+  // After patch_new: the lanes holding token tn's codes store them at kd / vd.
+  static __device__ __forceinline__ void store_new(const Buf& b, int tn, Elem* kd, Elem* vd) {
+    const int l = lane_id_here(), i = l & 15, c = l >> 4;
+    const int t = tn & 15;
+    if (i == t)
+#pragma unroll
+      for (int j = 0; j < KV; ++j) st16(kd + KB * c + 16 * j, tn >= 16 ? b.k[1][j] : b.k[0][j]);
+    if (c == (t >> 2)) {
+      VRaw x = b.v[0][0];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * u + 4 * c + r == tn) x = b.v[u][r];
+      *reinterpret_cast<VRaw*>(vd + VW * i) = x;
     }
   }
 

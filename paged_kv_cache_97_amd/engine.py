@@ -2,13 +2,14 @@
 
 Each step (gaoleia.github.io "PagedAttention 和 Continuous Batching" §2.3-§2.6;
 5688vip.com "vLLM核心机制" §3.3): the scheduler picks the rows; the engine
-moves swapped blocks (pkv_swap_blocks), writes the rows' new K/V into the
-paged pools (pkv_write_new_tokens) and runs attention over them
-(pkv_paged_attention_decode when every row is a single token, else
-pkv_paged_attention_varlen).  There is no model: every request's query, key
-and value rows are seeded synthetic values that depend only on (seed,
-request, position) -- a gather from a device-resident token bank -- so a
-token recomputed after a preemption gets the same K/V.  The path's work runs
+moves swapped blocks (pkv_swap_blocks), then either runs pkv_decode_step
+(every row a single token: the new K/V are written inside the decode
+attention launch) or writes the rows' new K/V into the paged pools
+(pkv_write_new_tokens) and runs pkv_paged_attention_varlen.  There is no
+model: every request's query, key and value rows are seeded synthetic values
+that depend only on (seed, request, position) -- a gather from a
+device-resident token bank -- so a token recomputed after a preemption gets
+the same K/V.  The path's work runs
 in the library's kernels.
 """
 from __future__ import annotations
@@ -116,21 +117,22 @@ class Engine:
         bs = self.cfg.block_size
         max_q = int(np.diff(qsl).max())
         max_len = int(sl.max())
-        if self.kv == "fp8":
+        if max_q == 1:
+            # every row is one decode token at position seq_len - 1: one call
+            # writes the new K/V and attends
+            if self.kv == "fp8":
+                out = ops.decode_step_fp8(tq, tk, tv, self.key_cache, self.value_cache, tbt, tsl, self.scale,
+                                          max_len, self.k_scale, self.v_scale)
+            else:
+                out = ops.decode_step(tq, tk, tv, self.key_cache, self.value_cache, tbt, tsl, self.scale, max_len)
+        elif self.kv == "fp8":
             ops.write_new_tokens_fp8(tbt, tpos, tqsl, bs, tk, tv, self.key_cache, self.value_cache, self.k_scale,
                                      self.v_scale)
-            if max_q == 1:
-                out = ops.paged_attention_decode_fp8(tq, self.key_cache, self.value_cache, tbt, tsl, self.scale,
-                                                     max_len, self.k_scale, self.v_scale)
-            else:
-                out = ops.paged_attention_varlen_fp8(tq, self.key_cache, self.value_cache, tbt, tsl, tqsl, self.scale,
-                                                     max_q, max_len, self.k_scale, self.v_scale)
+            out = ops.paged_attention_varlen_fp8(tq, self.key_cache, self.value_cache, tbt, tsl, tqsl, self.scale,
+                                                 max_q, max_len, self.k_scale, self.v_scale)
         else:
             ops.write_new_tokens(tbt, tpos, tqsl, bs, tk, tv, self.key_cache, self.value_cache)
-            if max_q == 1:
-                out = ops.paged_attention_decode(tq, self.key_cache, self.value_cache, tbt, tsl, self.scale, max_len)
-            else:
-                out = ops.paged_attention_varlen(tq, self.key_cache, self.value_cache, tbt, tsl, tqsl, self.scale,
-                                                 max_q, max_len)
+            out = ops.paged_attention_varlen(tq, self.key_cache, self.value_cache, tbt, tsl, tqsl, self.scale,
+                                             max_q, max_len)
         self.sched.complete(plan)
         return StepOutput(plan, out, qsl)

@@ -46,6 +46,11 @@ _SIGNATURES = {
     "pkv_paged_attention_varlen_fp8": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,
                                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
                                                 _c_f32, _c_f32, _c_f32, _c_vp, _c_sz, _c_vp]),
+    "pkv_decode_step": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32, _c_i32,
+                                 _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_f32, _c_i32, _c_vp, _c_sz, _c_vp]),
+    "pkv_decode_step_fp8": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32,
+                                     _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_f32, _c_f32, _c_f32, _c_vp,
+                                     _c_sz, _c_vp]),
     "pkv_copy_blocks": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp]),
     "pkv_swap_blocks": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_vp]),
     "pkv_set_profile_events": (_c_i32, [_c_vp, _c_vp]),
@@ -314,6 +319,68 @@ def paged_attention_decode_fp8(query: torch.Tensor, key_cache: torch.Tensor, val
         block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32, 1), B, Hq, Hkv, D, NB, bs,
         int(max_seq_len), float(scale), float(k_scale), float(v_scale), _dev(ws, "workspace"),
         ws.numel() * ws.element_size(), _stream(query)), "paged_attention_decode_fp8")
+    return out
+
+
+def _step_rows(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor) -> None:
+    B, Hq, D = query.shape
+    if key.shape != (B, key_cache.shape[2], D) or value.shape != key.shape:
+        raise ValueError("key/value must be [num_seqs, num_kv_heads, head_dim]")
+    if key.dtype != query.dtype or value.dtype != query.dtype:
+        raise ValueError("key/value must have the query's dtype")
+
+
+def decode_step(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                value_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                max_seq_len: int, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step: write each sequence's new token (position seq_lens[s]-1,
+    rows key[s]/value[s]) into its slot, then decode attention; float32 [B, Hq, D]."""
+    B, Hq, D = query.shape
+    NB, bs, Hkv, Dk = key_cache.shape
+    if Dk != D or value_cache.shape != key_cache.shape:
+        raise ValueError("cache shapes disagree with the query")
+    if query.dtype != key_cache.dtype or value_cache.dtype != key_cache.dtype:
+        raise ValueError("query and caches must share one dtype")
+    if block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_tables/seq_lens must have num_seqs rows")
+    _step_rows(query, key, value, key_cache)
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=query.device)
+    ws = _workspace(decode_workspace_size(B, Hq, Hkv, D, bs, query.dtype), query.device, workspace)
+    _check(lib().pkv_decode_step(
+        _dev(out, "out", torch.float32, 3), _dev(query, "query", ndim=3), _dev(key, "key", ndim=3),
+        _dev(value, "value", ndim=3), _dev(key_cache, "key_cache", ndim=4), _dev(value_cache, "value_cache", ndim=4),
+        _dev(block_tables, "block_tables", torch.int32, 2), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens", torch.int32, 1), B, Hq, Hkv, D, NB, bs, int(max_seq_len), float(scale),
+        _kv_dtype(query), _dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream(query)), "decode_step")
+    return out
+
+
+def decode_step_fp8(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                    value_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                    max_seq_len: int, k_scale: float, v_scale: float, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """decode_step over E4M3 pools: bf16 query/key/value, quantising write, E4M3 attention."""
+    B, Hq, D = query.shape
+    _fp8_pools(key_cache, value_cache)
+    NB, bs, Hkv, Dk = key_cache.shape
+    if Dk != D or query.dtype != torch.bfloat16:
+        raise ValueError("query must be bfloat16 [B, Hq, D] matching the pools")
+    if block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_tables/seq_lens must have num_seqs rows")
+    _step_rows(query, key, value, key_cache)
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=query.device)
+    nbytes = int(lib().pkv_decode_workspace_size(B, Hq, Hkv, D, bs, PKV_FP8_E4M3))
+    ws = _workspace(nbytes, query.device, workspace)
+    _check(lib().pkv_decode_step_fp8(
+        _dev(out, "out", torch.float32, 3), _dev(query, "query", ndim=3), _dev(key, "key", ndim=3),
+        _dev(value, "value", ndim=3), _dev(key_cache, "key_cache", ndim=4), _dev(value_cache, "value_cache", ndim=4),
+        _dev(block_tables, "block_tables", torch.int32, 2), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens", torch.int32, 1), B, Hq, Hkv, D, NB, bs, int(max_seq_len), float(scale),
+        float(k_scale), float(v_scale), _dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream(query)),
+        "decode_step_fp8")
     return out
 
 

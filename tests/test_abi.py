@@ -130,3 +130,30 @@ def test_fp8_validation_runs_before_any_launch():
                                             10, 16, 64, 0.1, float("nan"), 1.0, ctypes.c_void_p(1 << 20), 1 << 30,
                                             None)
     assert st == 1 and b"scale" in lib.pkv_last_error()
+
+
+def _step(lib, fp8=False, **kw):
+    args = dict(out=1 << 20, query=1 << 20, key=1 << 20, value=1 << 20, kc=1 << 20, vc=1 << 20, bt=1 << 20,
+                max_blocks=4, seq_lens=1 << 20, B=2, Hq=8, Hkv=2, D=128, NB=16, bs=16, max_len=64, scale=0.1,
+                dtype=1, k_scale=0.5, v_scale=0.25, ws=1 << 20, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    head = [args[k] for k in ("out", "query", "key", "value", "kc", "vc", "bt", "max_blocks", "seq_lens", "B", "Hq",
+                              "Hkv", "D", "NB", "bs", "max_len", "scale")]
+    tail = [args["ws"], args["ws_bytes"], args["stream"]]
+    if fp8:
+        return lib.pkv_decode_step_fp8(*head, args["k_scale"], args["v_scale"], *tail)
+    return lib.pkv_decode_step(*head, args["dtype"], *tail)
+
+
+@pytest.mark.parametrize("fp8,kw,code", [
+    (False, dict(key=None), 1), (False, dict(value=None), 1), (False, dict(key=(1 << 20) + 8), 1),
+    (False, dict(dtype=2), 1), (False, dict(D=96), 2), (False, dict(out=None), 1), (False, dict(ws_bytes=10), 3),
+    (False, dict(B=0, key=None, value=None), 0),
+    (True, dict(k_scale=0.0), 1), (True, dict(v_scale=float("nan")), 1), (True, dict(value=None), 1),
+    (True, dict(Hq=7), 1), (True, dict(B=0), 0),
+])
+def test_decode_step_validation_runs_before_any_launch(fp8, kw, code):
+    lib = ops.lib()
+    assert _step(lib, fp8, **kw) == code
+    if code:
+        assert lib.pkv_last_error()
