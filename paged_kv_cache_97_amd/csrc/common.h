@@ -55,6 +55,20 @@ __device__ __forceinline__ float wave_max_across_rows(float v) {
   return v;
 }
 
+// The same maximum with the gfx950 row-swap permutes: permlane16_swap pairs
+// row r with row r ^ 1 and permlane32_swap the two 32-lane halves.  Each
+// returns both swapped registers; whichever holds which, every lane finds its
+// own value and its partner's among the two, so a max over both is the
+// pairwise max.  VALU only: no LDS round trip on the softmax critical path.
+__device__ __forceinline__ float wave_max_across_rows_swap(float v) {
+  const uint32_t x = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t y = __float_as_uint(m);
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ float wave_sum_across_rows(float v) {
   v += __shfl_xor(v, 16);
   v += __shfl_xor(v, 32);

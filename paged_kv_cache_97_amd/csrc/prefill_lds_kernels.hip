@@ -129,7 +129,9 @@ prefill_lds_kernel(const PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][32 * RB];       // [buffer][32 token rows]
   __shared__ __attribute__((aligned(16))) uint8_t vtbuf[2][D * VT];       // [buffer][128 dim rows]
   __shared__ int s_item;
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, col = l & 15, c = l >> 4;
+  // wave is read through readfirstlane so the compiler knows every per-wave
+  // decision below is uniform: scalar branches, no exec-masked loop exits.
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), l = tid & 63, col = l & 15, c = l >> 4;
   const int B = a.num_seqs, G = a.group, Hkv = a.num_kv_heads, Hq = a.num_q_heads;
   const int max_tok = a.max_blocks * BS;
   const int* plan = a.plan;
@@ -192,25 +194,30 @@ prefill_lds_kernel(const PrefillArgs a) {
     // Loader (bf16): piece k of this thread is 16 bytes (8 dims) of row ld_row
     // of the K chunk (k = 0) and of row lv_row of the V chunk (k = 1).  FP8:
     // waves 0-3 load K (row tid >> 3, 16 dims), waves 4-7 V (row lane & 31,
-    // 16 dims).  Rows past p_max load zeros.
-    u32x4 R[2];
-    const bool kthr = tid < kPfThreads / 2;            // FP8 only: this wave loads K
-    auto load_chunk = [&](int ch) {
+    // 16 dims).  Two register sets: chunk j travels in set j & 1, so chunks
+    // ch + 1 and ch + 2 are in flight while chunk ch is computed.  The loads
+    // are unconditional (block ids are
+    // clamped to the sequence's blocks, so every address is inside the pool)
+    // which keeps the wait before a store at "all but the newest loads";
+    // V rows past p_max are zeroed when stored, K rows past it only ever meet
+    // masked scores.
+    u32x4 S[2][2];
+    const bool kthr = wave < kPfWaves / 2;             // FP8 only: this wave loads K
+    auto load_chunk = [&](int ch, u32x4* R) {
       const int lb0 = (ch * 32) / BS;                          // uniform
       const int b0 = win.get(lb0);
       const int b1 = BS == 16 ? win.get(lb0 + 1) : b0;
-      auto fetch = [&](const Elem* pool, int r, int elem_off) {
-        const int tok = ch * 32 + r;
+      auto addr = [&](const Elem* pool, int r, int elem_off) {
         const int blk = BS == 16 && r >= 16 ? b1 : b0;
-        const int off = tok - (BS == 16 ? lb0 + (r >> 4) : lb0) * BS;
-        const Elem* base = pool + ((int64_t)blk * BS + off) * Hkv * D + h * D + elem_off;
-        return tok <= p_max ? ld16(base) : u32x4{0, 0, 0, 0};
+        const int off = BS == 16 ? (r & 15) : r;
+        return pool + ((int64_t)blk * BS + off) * Hkv * D + h * D + elem_off;
       };
       if constexpr (FP8) {
-        R[0] = kthr ? fetch(kc, tid >> 3, 16 * (tid & 7)) : fetch(vc, lane_id() & 31, 16 * ((tid - kPfThreads / 2) >> 5));
+        const int kr = tid >> 3, vr = lane_id() & 31;
+        R[0] = ld16(kthr ? addr(kc, kr, 16 * (tid & 7)) : addr(vc, vr, 16 * ((tid - kPfThreads / 2) >> 5)));
       } else {
-        R[0] = fetch(kc, ld_row, 8 * ld_chunk);
-        R[1] = fetch(vc, lv_row, 8 * lv_chunk);
+        R[0] = ld16(addr(kc, ld_row, 8 * ld_chunk));
+        R[1] = ld16(addr(vc, lv_row, 8 * lv_chunk));
       }
     };
     // V rows go in transposed: lanes 2m and 2m+1 hold tokens 2m, 2m+1; they
@@ -231,13 +238,15 @@ prefill_lds_kernel(const PrefillArgs a) {
         *reinterpret_cast<uint32_t*>(&vtbuf[b][dim * VT + tok2]) = word;
       }
     };
-    auto store_chunk = [&](int b) {
+    auto store_chunk = [&](int ch, int b, const u32x4* R) {
       if constexpr (FP8) {
+        const bool vpast = !kthr && ch * 32 + (lane_id() & 31) > p_max;
+        const u32x4 x = vpast ? u32x4{0, 0, 0, 0} : R[0];
         uint32_t d[8];                                 // 16 elements widened to bf16 pairs
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          d[2 * q4] = fp8x2_to_bf16x2(R[0][q4], false);
-          d[2 * q4 + 1] = fp8x2_to_bf16x2(R[0][q4], true);
+          d[2 * q4] = fp8x2_to_bf16x2(x[q4], false);
+          d[2 * q4 + 1] = fp8x2_to_bf16x2(x[q4], true);
         }
         if (kthr) {
           const int row = tid >> 3, p = tid & 7;
@@ -249,7 +258,8 @@ prefill_lds_kernel(const PrefillArgs a) {
         }
       } else {
         *reinterpret_cast<u32x4*>(&kbuf[b][ld_row * RB + ((ld_chunk ^ (ld_row & 15)) << 4)]) = R[0];
-        const uint32_t d[4] = {R[1][0], R[1][1], R[1][2], R[1][3]};
+        const u32x4 v = ch * 32 + lv_row > p_max ? u32x4{0, 0, 0, 0} : R[1];
+        const uint32_t d[4] = {v[0], v[1], v[2], v[3]};
         store_vt(b, lv_row, 8 * lv_chunk, d, std::integral_constant<int, 4>{});
       }
     };
@@ -297,7 +307,7 @@ prefill_lds_kernel(const PrefillArgs a) {
             if constexpr (DIAG) sc[t][u][r] = (ch * 32 + 16 * u + 4 * c + r <= pos[t]) ? sc[t][u][r] : -INFINITY;
             cmax = fmaxf(cmax, sc[t][u][r]);
           }
-        cmx[t] = wave_max_across_rows(cmax) * a.scale_log2;
+        cmx[t] = wave_max_across_rows_swap(cmax) * a.scale_log2;
       }
     };
     // Phase B: weights against the current reference maxima, then O^T += V^T P^T.
@@ -332,39 +342,51 @@ prefill_lds_kernel(const PrefillArgs a) {
     };
 
     const int nch = (p_max + 32) / 32;
-    load_chunk(0);
-    store_chunk(0);
+    load_chunk(0, S[0]);
+    load_chunk(1, S[1]);
+    store_chunk(0, 0, S[0]);
+    load_chunk(2, S[0]);
     __syncthreads();
-    // The hot loop touches O only through MFMAs.  When a column's maximum
+    // One chunk: scores from LDS buffer P (= ch & 1); when a column's maximum
     // outgrows its reference by more than the slack (always on the first
-    // chunk), the wave leaves the loop before the chunk's PV and barrier,
-    // rescales in the outer loop, and re-enters at the same chunk.
-    int ch = 0;
-    while (true) {
-      for (; ch < nch; ++ch) {
-        if (ch + 1 < nch) load_chunk(ch + 1);
-        if (has && ch * 32 <= p_max_w) {
-          if (ch * 32 + 31 > p_min_w) scores(ch & 1, ch, std::true_type{});
-          else scores(ch & 1, ch, std::false_type{});
-          bool need = false;
+    // chunk) the wave rescales first (a rare, wave-uniform branch); then PV,
+    // chunk ch + 1 (register set 1 - P, loaded two steps ago) into LDS buffer
+    // 1 - P, the same set reloaded at once with chunk ch + 3, barrier.  A set
+    // is never idle between its store and its reload, and its loads have two
+    // steps to land.
+    auto step = [&](int ch, auto par_tag) {
+      constexpr int P = decltype(par_tag)::value;
+      if (has && ch * 32 <= p_max_w) {
+        if (ch * 32 + 31 > p_min_w) scores(P, ch, std::true_type{});
+        else scores(P, ch, std::false_type{});
+        bool need = false;
 #pragma unroll
-          for (int t = 0; t < kPfTiles; ++t) need |= cmx[t] > mref[t] + kRescaleSlack;
-          if (__any(need)) break;
-          accumulate(ch & 1);
+        for (int t = 0; t < kPfTiles; ++t) need |= cmx[t] > mref[t] + kRescaleSlack;
+        if (__any(need)) {
+#pragma unroll
+          for (int t = 0; t < kPfTiles; ++t) {
+            const bool nt = cmx[t] > mref[t] + kRescaleSlack;
+            const float alpha = nt ? fast_exp2(mref[t] - cmx[t]) : 1.f;   // 0 on the first chunk
+            mref[t] = nt ? cmx[t] : mref[t];
+            lsum[t] *= alpha;
+#pragma unroll
+            for (int d = 0; d < NDT; ++d) o[t][d] *= alpha;
+          }
         }
-        if (ch + 1 < nch) store_chunk((ch + 1) & 1);
-        __syncthreads();
+        accumulate(P);
       }
-      if (ch >= nch) break;
-#pragma unroll
-      for (int t = 0; t < kPfTiles; ++t) {
-        const bool need = cmx[t] > mref[t] + kRescaleSlack;
-        const float alpha = need ? fast_exp2(mref[t] - cmx[t]) : 1.f;   // 0 on the first chunk
-        mref[t] = need ? cmx[t] : mref[t];
-        lsum[t] *= alpha;
-#pragma unroll
-        for (int d = 0; d < NDT; ++d) o[t][d] *= alpha;
-      }
+      // Past the last chunk the loads and stores are clamped and unused; the
+      // buffer stored into was last read before the previous barrier.
+      store_chunk(ch + 1, 1 - P, S[1 - P]);
+      load_chunk(ch + 3, S[1 - P]);
+      __syncthreads();
+    };
+    // Even and odd chunks alternate in straight-line code (an odd step past
+    // the last chunk computes nothing), so the compiler's wait counting sees
+    // which register set is older and waits only for it.
+    for (int ch = 0; ch < nch; ch += 2) {
+      step(ch, std::integral_constant<int, 0>{});
+      step(ch + 1, std::integral_constant<int, 1>{});
     }
 
 #pragma unroll
