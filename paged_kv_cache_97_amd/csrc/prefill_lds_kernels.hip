@@ -125,9 +125,12 @@ __global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu
 prefill_lds_kernel(const PrefillArgs a) {
   typedef TileBf16<128, BS> Tile;
   constexpr int D = 128, NDT = 8, RB = 256;            // row bytes of one KV head
-  constexpr int VT = 72;                               // bytes per dim row of the transposed V tile
+  // V is token-major like K, rows padded to 288 bytes: the transposing LDS
+  // reads of the PV operand then hit every bank pair at most twice and their
+  // per-dim-tile addresses are immediate offsets.
+  constexpr int VR = 288;
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][32 * RB];       // [buffer][32 token rows]
-  __shared__ __attribute__((aligned(16))) uint8_t vtbuf[2][D * VT];       // [buffer][128 dim rows]
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][32 * VR];       // [buffer][32 token rows]
   __shared__ int s_item;
   // wave is read through readfirstlane so the compiler knows every per-wave
   // decision below is uniform: scalar branches, no exec-masked loop exits.
@@ -143,8 +146,7 @@ prefill_lds_kernel(const PrefillArgs a) {
   const Elem* kc = reinterpret_cast<const Elem*>(a.key_cache);
   const Elem* vc = reinterpret_cast<const Elem*>(a.value_cache);
   const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.query);
-  const int ld_row = tid >> 4, ld_chunk = tid & 15;    // K loader: 16 lanes per 256 B row (32 rows)
-  const int lv_row = tid & 31, lv_chunk = tid >> 5;    // V loader: 32 lanes per 16 B column
+  const int ld_row = tid >> 4, ld_chunk = tid & 15;    // loader: 16 lanes per 256 B row (32 rows)
 
   while (true) {
     __syncthreads();                                   // everyone has read the previous item
@@ -192,9 +194,8 @@ prefill_lds_kernel(const PrefillArgs a) {
     win.fill(0);
 
     // Loader (bf16): piece k of this thread is 16 bytes (8 dims) of row ld_row
-    // of the K chunk (k = 0) and of row lv_row of the V chunk (k = 1).  FP8:
-    // waves 0-3 load K (row tid >> 3, 16 dims), waves 4-7 V (row lane & 31,
-    // 16 dims).  Two register sets: chunk j travels in set j & 1, so chunks
+    // of the K chunk (k = 0) and of the V chunk (k = 1).  FP8: waves 0-3 load
+    // K, waves 4-7 V (row (tid >> 3) & 31, 16 dims).  Two register sets: chunk j travels in set j & 1, so chunks
     // ch + 1 and ch + 2 are in flight while chunk ch is computed.  The loads
     // are unconditional (block ids are
     // clamped to the sequence's blocks, so every address is inside the pool)
@@ -213,34 +214,16 @@ prefill_lds_kernel(const PrefillArgs a) {
         return pool + ((int64_t)blk * BS + off) * Hkv * D + h * D + elem_off;
       };
       if constexpr (FP8) {
-        const int kr = tid >> 3, vr = lane_id() & 31;
-        R[0] = ld16(kthr ? addr(kc, kr, 16 * (tid & 7)) : addr(vc, vr, 16 * ((tid - kPfThreads / 2) >> 5)));
+        R[0] = ld16(addr(kthr ? kc : vc, (tid >> 3) & 31, 16 * (tid & 7)));
       } else {
         R[0] = ld16(addr(kc, ld_row, 8 * ld_chunk));
-        R[1] = ld16(addr(vc, lv_row, 8 * lv_chunk));
-      }
-    };
-    // V rows go in transposed: lanes 2m and 2m+1 hold tokens 2m, 2m+1; they
-    // swap dwords (DPP quad_perm [1,0,3,2]) and write whole dwords (token
-    // pair, one dim): the even lane dims 2w, the odd lane dims 2w + 1.
-    auto store_vt = [&](int b, int tok, int dim0, const uint32_t* d, auto nw_tag) {
-      constexpr int NW = decltype(nw_tag)::value;      // dwords (dim pairs) of this lane's token
-      const bool odd = tok & 1;
-      const int tok2 = (tok & ~1) * 2;                 // byte offset of the token pair
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const uint32_t mine = d[w];
-        const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)mine, 0xB1, 0xF, 0xF, true);
-        // even: (mine.lo, other.lo) = dim 2w of tokens (2m, 2m+1); odd: (other.hi, mine.hi) = dim 2w + 1
-        const uint32_t word = odd ? __builtin_amdgcn_perm(mine, other, 0x07060302u)
-                                  : __builtin_amdgcn_perm(other, mine, 0x05040100u);
-        const int dim = dim0 + 2 * w + (odd ? 1 : 0);
-        *reinterpret_cast<uint32_t*>(&vtbuf[b][dim * VT + tok2]) = word;
+        R[1] = ld16(addr(vc, ld_row, 8 * ld_chunk));
       }
     };
     auto store_chunk = [&](int ch, int b, const u32x4* R) {
       if constexpr (FP8) {
-        const bool vpast = !kthr && ch * 32 + (lane_id() & 31) > p_max;
+        const int row = (tid >> 3) & 31, p = tid & 7;
+        const bool vpast = !kthr && ch * 32 + row > p_max;
         const u32x4 x = vpast ? u32x4{0, 0, 0, 0} : R[0];
         uint32_t d[8];                                 // 16 elements widened to bf16 pairs
 #pragma unroll
@@ -249,27 +232,29 @@ prefill_lds_kernel(const PrefillArgs a) {
           d[2 * q4 + 1] = fp8x2_to_bf16x2(x[q4], true);
         }
         if (kthr) {
-          const int row = tid >> 3, p = tid & 7;
           *reinterpret_cast<u32x4*>(&kbuf[b][row * RB + (((2 * p) ^ (row & 15)) << 4)]) = u32x4{d[0], d[1], d[2], d[3]};
           *reinterpret_cast<u32x4*>(&kbuf[b][row * RB + (((2 * p + 1) ^ (row & 15)) << 4)]) =
               u32x4{d[4], d[5], d[6], d[7]};
         } else {
-          store_vt(b, lane_id() & 31, 16 * ((tid - kPfThreads / 2) >> 5), d, std::integral_constant<int, 8>{});
+          *reinterpret_cast<u32x4*>(&vbuf[b][row * VR + 32 * p]) = u32x4{d[0], d[1], d[2], d[3]};
+          *reinterpret_cast<u32x4*>(&vbuf[b][row * VR + 32 * p + 16]) = u32x4{d[4], d[5], d[6], d[7]};
         }
       } else {
         *reinterpret_cast<u32x4*>(&kbuf[b][ld_row * RB + ((ld_chunk ^ (ld_row & 15)) << 4)]) = R[0];
-        const u32x4 v = ch * 32 + lv_row > p_max ? u32x4{0, 0, 0, 0} : R[1];
-        const uint32_t d[4] = {v[0], v[1], v[2], v[3]};
-        store_vt(b, lv_row, 8 * lv_chunk, d, std::integral_constant<int, 4>{});
+        *reinterpret_cast<u32x4*>(&vbuf[b][ld_row * VR + 16 * ld_chunk]) =
+            ch * 32 + ld_row > p_max ? u32x4{0, 0, 0, 0} : R[1];
       }
     };
 
-    float mref[kPfTiles], lsum[kPfTiles];
-    f32x4 o[kPfTiles][NDT];
+    // osum: the softmax denominators, accumulated by the MFMA against an
+    // all-ones A tile (every row of it is the column's sum of the bf16 weights
+    // that multiply V), so the VALU does no per-element adds.
+    float mref[kPfTiles];
+    f32x4 o[kPfTiles][NDT], osum[kPfTiles];
 #pragma unroll
     for (int t = 0; t < kPfTiles; ++t) {
       mref[t] = -INFINITY;
-      lsum[t] = 0.f;
+      osum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int d = 0; d < NDT; ++d) o[t][d] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -312,28 +297,34 @@ prefill_lds_kernel(const PrefillArgs a) {
     };
     // Phase B: weights against the current reference maxima, then O^T += V^T P^T.
     // Row i of O^T tile dt is dim i + 16 dt; k-slot 4u + r is token 16u + 4c + r,
-    // the order in which the S^T accumulator holds P.
+    // the order in which the S^T accumulator holds P.  The A operand comes
+    // from two transposing LDS reads (ds_read_b64_tr_b16): within each
+    // 16-lane group, lane i receives element k = element (i & 3) of the
+    // 8 bytes read by lane 4k + (i >> 2).  Lane j of group c reads token
+    // 16u + 4c + (j >> 2), dims 16 dt + 4 (j & 3) .. + 3, so lane i gets
+    // dim 16 dt + i of tokens 16u + 4c .. + 3: k-slots 4u .. 4u + 3.
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
     auto accumulate = [&](int b) {
-      const uint8_t* Vt = vtbuf[b];
+      const uint8_t* vlane = vbuf[b] + (4 * c + (col >> 2)) * VR + 8 * (col & 3);
       bf16x8 pb[kPfTiles];
+      constexpr uint32_t kOnes = 0x3F803F80u;           // two bf16 1.0
 #pragma unroll
       for (int t = 0; t < kPfTiles; ++t) {
-        float ps = 0.f;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = fast_exp2(fmaf(sc[t][u][r], a.scale_log2, -mref[t]));
-            ps += p;
-            pb[t][4 * u + r] = (__bf16)p;
-          }
-        lsum[t] += ps;
+          for (int r = 0; r < 4; ++r)
+            pb[t][4 * u + r] = (__bf16)fast_exp2(fmaf(sc[t][u][r], a.scale_log2, -mref[t]));
+        osum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u32x4{kOnes, kOnes, kOnes, kOnes}),
+                                                         pb[t], osum[t], 0, 0, 0);
       }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const uint8_t* vrow = Vt + (col + 16 * dt) * VT;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 8 * c);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 32 + 8 * c);
+        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                      (lds_v4i16*)(vlane + 32 * dt)));
+        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                      (lds_v4i16*)(vlane + 16 * VR + 32 * dt)));
         const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int t = 0; t < kPfTiles; ++t)
@@ -368,7 +359,7 @@ prefill_lds_kernel(const PrefillArgs a) {
             const bool nt = cmx[t] > mref[t] + kRescaleSlack;
             const float alpha = nt ? fast_exp2(mref[t] - cmx[t]) : 1.f;   // 0 on the first chunk
             mref[t] = nt ? cmx[t] : mref[t];
-            lsum[t] *= alpha;
+            osum[t] *= alpha;
 #pragma unroll
             for (int d = 0; d < NDT; ++d) o[t][d] *= alpha;
           }
@@ -391,7 +382,7 @@ prefill_lds_kernel(const PrefillArgs a) {
 
 #pragma unroll
     for (int t = 0; t < kPfTiles; ++t) {
-      const float tot = wave_sum_across_rows(lsum[t]);
+      const float tot = osum[t][0];                    // every row holds the column sum
       const int f = f0w + 16 * t + col;
       if (f >= f1w) continue;
       const int row = f / G, head = f - row * G;
