@@ -252,7 +252,7 @@ def bench_serve(args) -> int:
     cfg = SchedulerConfig(block_size=16, num_gpu_blocks=16384, max_num_seqs=128, max_num_batched_tokens=2048,
                           max_prefill_chunk=512, watermark=0.01)
     eng = Engine(cfg, 64, 8, 128, seed=1, kv_cache_dtype="fp8" if fp8 else "bf16",
-                 k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
+                 k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE, scheduler=args.scheduler)
     for rid, p, g, _ in W.request_mix(1, 512, prompt=("lognormal", 1500.0, W.LOGNORMAL_SIGMA, 16, 8192),
                                       new_tokens=("uniform", 32, 256)):
         eng.add_request(rid, p, g)
@@ -281,7 +281,7 @@ def bench_serve(args) -> int:
         "dtype": "fp8-e4m3 KV, bf16 Q" if fp8 else "bf16", "data": "synthetic",
         "config": {"workload": "serve-512req-lognormal1500-new32to256-h64x8-d128",
                    "max_num_seqs": 128, "max_num_batched_tokens": 2048, "prefill_chunk": 512,
-                   "pool_blocks": 16384},
+                   "pool_blocks": 16384, "scheduler": args.scheduler},
         "decode_tokens_per_s": round(dec / wall, 1), "prefill_rows": pre_rows, "preemptions": preempt,
         "host_ms_per_step": round(1e3 * host / max(1, args.steps), 4),
     }
@@ -305,6 +305,8 @@ def main() -> int:
                     help="auto: pools in the workload's dtype; fp8: OCP E4M3 pools (k/v scales %g/%g)" % (0.0125, 0.02))
     ap.add_argument("--serve", action="store_true",
                     help="run the continuous-batching step driver over a synthetic request stream instead")
+    ap.add_argument("--scheduler", choices=["native", "python"], default="native",
+                    help="--serve: the native (C++) scheduler or the Python one it mirrors")
     ap.add_argument("--two-call", action="store_true",
                     help="decode: time write_new_tokens + paged_attention_decode instead of the one-call decode_step")
     ap.add_argument("--blocks", action="store_true",

@@ -2,7 +2,8 @@
 
     python -m paged_kv_cache_97_amd.build_lib [-v]
 
-Each .hip source is compiled to an object in parallel, then linked into
+Each .hip source is compiled with hipcc (and each host-only .cpp source with
+the host C++ compiler) to an object in parallel, then linked into
 paged_kv_cache_97_amd/libpagedkv.so (replaced atomically).
 """
 from __future__ import annotations
@@ -20,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 SOURCES = ["api.hip", "cache_kernels.hip", "decode_kernels.hip", "varlen_kernels.hip", "prefill_lds_kernels.hip",
-           "block_kernels.hip"]
+           "block_kernels.hip", "scheduler.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -37,16 +38,26 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpagedkv.so)")
 
 
+def cxx() -> str:
+    for cand in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("no host C++ compiler found")
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [cxx(), "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (r.stderr or "").splitlines()
                      if "packed-fp32-ops' is not a recognized feature" not in l)
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed for %s:\n%s" % (src, errs))
+        raise RuntimeError("%s failed for %s:\n%s" % (os.path.basename(cmd[0]), src, errs))
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
     return obj

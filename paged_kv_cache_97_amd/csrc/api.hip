@@ -562,3 +562,12 @@ int pkv_paged_attention_varlen_fp8(float* out, const void* query, const void* ke
 }
 
 }  // extern "C"
+
+// Status reporting for the library's host-only parts (the native scheduler).
+namespace pkv {
+int report(int status, const char* msg) {
+  if (status == PKV_OK) return ok();
+  return fail(status, "%s", msg);
+}
+}  // namespace pkv
+

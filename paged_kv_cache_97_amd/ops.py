@@ -51,6 +51,16 @@ _SIGNATURES = {
     "pkv_decode_step_fp8": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32,
                                      _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_f32, _c_f32, _c_f32, _c_vp,
                                      _c_sz, _c_vp]),
+    "pkv_sched_create": (_c_vp, [_c_vp, _c_vp]),
+    "pkv_sched_destroy": (None, [_c_vp]),
+    "pkv_sched_add_request": (_c_i32, [_c_vp, _c_i64, _c_i32, _c_i32]),
+    "pkv_sched_has_work": (_c_i32, [_c_vp]),
+    "pkv_sched_schedule": (_c_i32, [_c_vp, _c_vp]),
+    "pkv_sched_complete": (_c_i32, [_c_vp]),
+    "pkv_sched_num_free_gpu": (_c_i32, [_c_vp]),
+    "pkv_sched_num_free_cpu": (_c_i32, [_c_vp]),
+    "pkv_sched_count": (_c_i32, [_c_vp, _c_i32]),
+    "pkv_sched_request_info": (_c_i32, [_c_vp, _c_i64, _c_vp, _c_vp, _c_vp]),
     "pkv_copy_blocks": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp]),
     "pkv_swap_blocks": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_vp]),
     "pkv_set_profile_events": (_c_i32, [_c_vp, _c_vp]),

@@ -13,15 +13,19 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "pagedkv.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
     lib = ops.lib()
     names = _declared()
-    assert "pkv_paged_attention_decode" in names and len(names) >= 12
+    assert "pkv_paged_attention_decode" in names and "pkv_sched_schedule" in names and len(names) >= 12
     for n in names:
         assert hasattr(lib, n), n
         assert n in ops._SIGNATURES, "binding lacks " + n
