@@ -345,10 +345,19 @@ int pkv_swap_blocks(const void* src_key, const void* src_value, void* dst_key, v
  *
  * pkv_set_waves_per_cu: default worker density per compute unit (4..16,
  * multiple of 4; default 4).  Returns the previous value.
+ *
+ * pkv_set_decode_segment_cost: virtual chunks (0..64, default 0) the decode
+ * split charges for each (sequence, KV head) range a worker starts, so that
+ * workers crossing more ranges get fewer real chunks (a new range costs a
+ * dependent block-table load and a first-chunk round trip, about three
+ * chunks of streaming on MI355X).  0 splits by real chunks only.  Results
+ * do not depend on it beyond float reordering.  Returns the previous value
+ * (-1 for an out-of-range argument).
  */
 int pkv_set_profile_events(void* start_event, void* stop_event);
 int pkv_set_decode_workers(int32_t workers);
 int pkv_set_waves_per_cu(int32_t waves);
+int pkv_set_decode_segment_cost(int32_t chunks);
 int pkv_get_waves_per_cu(void);
 
 #ifdef __cplusplus

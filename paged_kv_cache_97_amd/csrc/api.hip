@@ -17,6 +17,7 @@ thread_local hipEvent_t g_ev_start = nullptr;
 thread_local hipEvent_t g_ev_stop = nullptr;
 std::atomic<int> g_workers_override{0};
 std::atomic<int> g_waves_per_cu{4};
+std::atomic<int> g_seg_chunks{0};
 
 constexpr int kMaxSeqs = 8192;
 
@@ -89,7 +90,7 @@ bool good_scale(float s) { return std::isfinite(s) && s > 0.f && std::isfinite(1
 // Upper bound of the chunk count the split sees, times the worker count, must
 // stay far inside int64 (the kernels multiply the two).
 bool split_fits(int64_t num_seqs, int64_t pairs_per_seq, int64_t max_tokens, int64_t workers) {
-  const int64_t chunks = num_seqs * pairs_per_seq * ((max_tokens + 31) / 32);
+  const int64_t chunks = num_seqs * pairs_per_seq * ((max_tokens + 31) / 32 + g_seg_chunks.load());
   return chunks < (int64_t(1) << 40) && workers <= 65536;
 }
 
@@ -118,6 +119,11 @@ int pkv_set_profile_events(void* start_event, void* stop_event) {
   g_ev_start = static_cast<hipEvent_t>(start_event);
   g_ev_stop = static_cast<hipEvent_t>(stop_event);
   return ok();
+}
+
+int pkv_set_decode_segment_cost(int32_t chunks) {
+  if (chunks < 0 || chunks > 64) return -1;
+  return g_seg_chunks.exchange(chunks);
 }
 
 int pkv_set_decode_workers(int32_t workers) {
@@ -357,6 +363,7 @@ static int run_decode(float* out, const void* query, const void* key_cache, cons
   a.scale_log2 = scale * fmt.k_scale * 1.4426950408889634f;
   a.v_scale = fmt.v_scale;
   a.workers = workers;
+  a.seg_chunks = g_seg_chunks.load();
   a.new_k = new_k;
   a.new_v = new_v;
   a.k_inv = fmt.kind == pkv::KvKind::FP8 ? 1.0f / fmt.k_scale : 1.0f;

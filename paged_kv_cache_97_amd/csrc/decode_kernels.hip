@@ -232,10 +232,12 @@ __device__ __forceinline__ int clamp_len(int L, int max_tok) {
   return L < 0 ? 0 : (L > max_tok ? max_tok : L);
 }
 
-// Chunks of sequence s that this launch handles (0 for skipped sequences).
+// Chunks of each pair of sequence s that this launch handles, plus the
+// pair's virtual start-up chunks (0 for skipped and empty sequences).
 __device__ __forceinline__ int seq_chunks(const DecodeArgs& a, int s, int max_tok) {
   if (a.qsl != nullptr && a.qsl[s + 1] - a.qsl[s] != 1) return 0;
-  return (clamp_len(a.seq_lens[s], max_tok) + 31) >> 5;
+  const int n = (clamp_len(a.seq_lens[s], max_tok) + 31) >> 5;
+  return n > 0 ? n + a.seg_chunks : 0;
 }
 
 template <class Tile>
@@ -269,7 +271,11 @@ decode_split_kernel(const DecodeArgs a) {
   int ch = (int)(local - (int64_t)pr * n_s);
   int64_t remaining = x1 - x0;
   while (true) {
+    // Positions count the pair's seg_chunks virtual chunks first: [ch, ch +
+    // seg) maps to the real chunks [r0, r1).
     const int seg = (int)min<int64_t>(n_s - ch, remaining);
+    const int n_real = n_s - a.seg_chunks;
+    const int r0 = max(ch - a.seg_chunks, 0), r1 = max(ch + seg - a.seg_chunks, 0);
     const int raw_len = uniform(a.seq_lens[s]);
     const int L = clamp_len(raw_len, max_tok);
     const int row = a.qsl ? uniform(a.qsl[s]) : s;
@@ -280,7 +286,7 @@ decode_split_kernel(const DecodeArgs a) {
     // token is read from the pool, as a separate write would leave it).
     int tn = -1;
     int64_t new_row = 0;
-    if (a.new_k != nullptr && ch + seg == n_s && raw_len == L) {
+    if (a.new_k != nullptr && r1 == n_real && r1 > r0 && raw_len == L) {
       const int lt = L - 1;
       const int phys = uniform(a.block_tables[(int64_t)s * a.max_blocks + lt / Tile::BS]);
       if (phys >= 0 && phys < a.num_blocks) {
@@ -288,8 +294,9 @@ decode_split_kernel(const DecodeArgs a) {
         new_row = (((int64_t)phys * Tile::BS + lt % Tile::BS) * a.num_kv_heads + h) * Tile::D;
       }
     }
-    run_segment<Tile>(a, s, row, h, ht, L, ch, ch + seg, ch == 0 && seg == n_s, (int64_t)s * ppseq + pr + w,
-                      tn, ht == 0, new_row);
+    if (r1 > r0)                                       // a range of virtual chunks only does nothing
+      run_segment<Tile>(a, s, row, h, ht, L, r0, r1, r0 == 0 && r1 == n_real, (int64_t)s * ppseq + pr + w, tn,
+                        ht == 0, new_row);
     remaining -= seg;
     if (remaining <= 0) break;
     ch = 0;
@@ -317,15 +324,16 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(const DecodeArgs a) 
   const int row = a.qsl ? a.qsl[s] : s;
   float* out = a.out + ((int64_t)row * a.num_q_heads + hq0) * D;
   const int B = a.num_seqs;
-  const int n_s = a.cum[s + 1] - a.cum[s];
+  const int n_s = a.cum[s + 1] - a.cum[s];             // real + virtual chunks per pair
   constexpr int Q4 = D / 4;
   if (n_s == 0) {
     for (int i = threadIdx.x; i < cols * Q4; i += 256) st16f(out + 4 * i, f32x4{0.f, 0.f, 0.f, 0.f});
     return;
   }
+  // the workers that hold the pair's real chunks (positions seg_chunks ..)
   const int64_t total = (int64_t)ppseq * a.cum[B];
-  const int64_t first = (int64_t)ppseq * a.cum[s] + (int64_t)pr * n_s;
-  const int64_t last = first + n_s - 1;
+  const int64_t first = (int64_t)ppseq * a.cum[s] + (int64_t)pr * n_s + a.seg_chunks;
+  const int64_t last = (int64_t)ppseq * a.cum[s] + (int64_t)pr * n_s + n_s - 1;
   const int64_t W = a.workers;
   // worker owning chunk x: the last i with floor(i * total / W) <= x
   const int i0 = (int)(((first + 1) * W - 1) / total);

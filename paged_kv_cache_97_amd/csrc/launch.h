@@ -33,6 +33,11 @@ struct DecodeArgs {
   float scale_log2;           // scale * log2(e) (times k_scale for FP8 pools)
   float v_scale;              // multiplies every output (FP8 pools; 1 otherwise)
   int workers;                // wavefronts sharing the work (split points)
+  // Virtual chunks charged at the start of every non-empty pair: the equal
+  // split of the work is made over real + virtual chunks, so a wave whose
+  // range crosses into a new pair (and pays the new pair's block-table and
+  // first-chunk latency) gets that many fewer real chunks.  0: plain split.
+  int seg_chunks;
   // Optional fused cache write (decode only, qsl == NULL): new_k / new_v
   // [B, Hkv, D] are the rows of each sequence's new token, position
   // seq_lens[s] - 1 (query element type: float32 for F32 pools, bfloat16

@@ -66,6 +66,7 @@ _SIGNATURES = {
     "pkv_set_profile_events": (_c_i32, [_c_vp, _c_vp]),
     "pkv_set_decode_workers": (_c_i32, [_c_i32]),
     "pkv_set_waves_per_cu": (_c_i32, [_c_i32]),
+    "pkv_set_decode_segment_cost": (_c_i32, [_c_i32]),
     "pkv_get_waves_per_cu": (_c_i32, []),
 }
 
@@ -480,6 +481,12 @@ def swap_blocks(src_key: torch.Tensor, src_value: Optional[torch.Tensor], dst_ke
 # ----------------------------------------------------------------- knobs and timing
 def set_decode_workers(n: int) -> int:
     return int(lib().pkv_set_decode_workers(int(n)))
+
+
+def set_decode_segment_cost(n: int) -> int:
+    """Virtual chunks the decode split charges per (sequence, KV head) range;
+    returns the previous value."""
+    return int(lib().pkv_set_decode_segment_cost(int(n)))
 
 
 def set_waves_per_cu(n: int) -> int:

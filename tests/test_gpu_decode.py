@@ -207,3 +207,20 @@ def test_fused_write_mixed_rows_and_padding(dev):
     assert int(slots[3]) == -1
     assert np.array_equal(slots.cpu().numpy(), r_slots)
     assert same_bits(t["key_cache"], r_kc) and same_bits(t["value_cache"], r_vc)
+
+
+@pytest.mark.parametrize("cost", [0, 1, 3, 7, 40])
+@pytest.mark.parametrize("workers", [0, 5, 333, 4096])
+def test_segment_cost_splits(cost, workers, dev):
+    """The split over real + virtual start-up chunks: every charge per pair,
+    from none to more than a short sequence's chunks, with few and many
+    workers (some of them holding only virtual chunks), matches the oracle."""
+    prev_w = ops.set_decode_workers(workers)
+    prev_c = ops.set_decode_segment_cost(cost)
+    try:
+        _check_full(W.generate(SMALL["gqa8-bs16"], seed=21), dev, "cost=%d workers=%d" % (cost, workers))
+        spec = W.reduced(3, num_decode=12, decode_len=("fixed", (1, 2, 31, 32, 33, 64, 65, 100, 1, 700, 3, 40)))
+        _check_full(W.generate(spec, seed=22), dev, "edges cost=%d workers=%d" % (cost, workers))
+    finally:
+        ops.set_decode_workers(prev_w)
+        ops.set_decode_segment_cost(prev_c)

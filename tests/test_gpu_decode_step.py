@@ -100,6 +100,16 @@ def test_step_equals_write_then_decode_bitwise(name, fp8, dev):
     _compare(W.generate(spec, seed=301), dev, fp8, name)
 
 
+@pytest.mark.parametrize("cost", [0, 7])
+def test_step_segment_costs_bitwise(cost, dev):
+    prev = ops.set_decode_segment_cost(cost)
+    try:
+        _compare(W.generate(SHAPES["gqa8-bs16"], seed=309), dev, False, "cost=%d" % cost)
+        _compare(W.generate(SHAPES["edges"], seed=310), dev, True, "cost=%d" % cost)
+    finally:
+        ops.set_decode_segment_cost(prev)
+
+
 @pytest.mark.parametrize("workers", [1, 2, 3, 7, 64, 333, 4096])
 def test_step_forced_split_points_bitwise(workers, dev):
     """Every way the split can cut the last chunk off (single-chunk ranges,
