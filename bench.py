@@ -138,9 +138,10 @@ def _fp8_sample(oracle, wl, kc, vc, s, scales):
 
 def _cpu_baseline(wl, budget_s: float = 12.0, fp8_scales=None):
     """Time the oracle's attention on the batch's sequences, one at a time in
-    batch order, until about budget_s of work is done; report the KV GB/s of
-    that sample (the same bytes model as the GPU value).  With fp8_scales the
-    oracle reads E4M3 pools (quantised per sequence outside the timed part)."""
+    batch order (wrapping round to the first sequence after the last), until
+    about budget_s of work is done; report the KV GB/s of that sample (the
+    same bytes model as the GPU value).  With fp8_scales the oracle reads E4M3
+    pools (quantised per sequence outside the timed part)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -152,12 +153,13 @@ def _cpu_baseline(wl, budget_s: float = 12.0, fp8_scales=None):
     decode = not wl.is_prefill.any()
     dt = 0.0
     done, tokens, rows = 0, 0, 0
-    while done < wl.num_seqs and dt < budget_s:
-        s = slice(done, done + 1)
-        r0, r1 = int(wl.query_start_loc[done]), int(wl.query_start_loc[done + 1])
+    while dt < budget_s:
+        i = done % wl.num_seqs
+        s = slice(i, i + 1)
+        r0, r1 = int(wl.query_start_loc[i]), int(wl.query_start_loc[i + 1])
         pk, pv, table, dts = kc, vc, wl.block_tables[s], wl.spec.dtype
         if fp8_scales is not None:
-            pk, pv, table = _fp8_sample(oracle, wl, kc, vc, done, fp8_scales)
+            pk, pv, table = _fp8_sample(oracle, wl, kc, vc, i, fp8_scales)
         t0 = time.perf_counter()
         if decode:
             oracle.decode_attention(wl.query[r0:r1], pk, pv, table, wl.seq_lens[s], wl.scale, dts, fp8_scales)
@@ -165,16 +167,18 @@ def _cpu_baseline(wl, budget_s: float = 12.0, fp8_scales=None):
             oracle.varlen_attention(wl.query[r0:r1], pk, pv, table, wl.seq_lens[s], np.array([0, r1 - r0]),
                                     wl.scale, dts, fp8_scales)
         dt += time.perf_counter() - t0
-        tokens += int(wl.seq_lens[done])
+        tokens += int(wl.seq_lens[i])
         rows += r1 - r0
         done += 1
     sp = wl.spec
     nbytes = tokens * 2 * sp.num_kv_heads * sp.head_dim * (1 if fp8_scales is not None else wl.elem_bytes)
+    passes, extra = divmod(done, wl.num_seqs)
+    covered = ("%d full pass%s over the %d sequences%s" % (passes, "" if passes == 1 else "es", wl.num_seqs,
+                                                          " plus the first %d" % extra if extra else "")
+               if passes else "the first %d of %d sequences" % (done, wl.num_seqs))
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": "float64 NumPy oracle %s%s attention over the first %d of %d sequences "
-                      "(%d query rows, %d KV tokens), %.1f s" % ("E4M3 " if fp8_scales else "",
-                                                                "decode" if decode else "varlen", done,
-                                                                wl.num_seqs, rows, tokens, dt),
+            "sample": "float64 NumPy oracle %s%s attention, %s (%d query rows, %d KV tokens), %.1f s"
+                      % ("E4M3 " if fp8_scales else "", "decode" if decode else "varlen", covered, rows, tokens, dt),
             "seq_tokens_per_s": round(rows / dt, 3)}
 
 
