@@ -116,6 +116,42 @@ prefill_plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__
   }
 }
 
+// max(a, b) as one v_max_f32.  The compiler's fmaxf quiets signalling NaNs
+// first (an extra v_max x, x per operand) when it cannot see where a value
+// came from, e.g. a cross-lane swap; the scores here are never NaN once masked.
+__device__ __forceinline__ float raw_max(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// Column maxima of two tiles at once.  a and b are each lane's maximum over
+// its rows of tile 0 and tile 1; the row-pair swap leaves every lane with two
+// values of one tile (which one depends only on the lane's row parity, and
+// `tile_of_lane` below says which), the half swap combines the two row pairs
+// of that tile.  Result: the column maximum over all 32 tokens of the lane's
+// tile, with two cross-lane steps for both tiles.
+__device__ __forceinline__ float pair_tile_max(float a, float b) {
+  const auto s1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const float z = raw_max(__uint_as_float(s1[0]), __uint_as_float(s1[1]));
+  const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+  return raw_max(__uint_as_float(s2[0]), __uint_as_float(s2[1]));
+}
+
+// The tile (0 or 1) whose maximum pair_tile_max leaves in this lane: the same
+// swap applied to the tile numbers themselves.
+__device__ __forceinline__ int tile_of_lane() {
+  return (int)__builtin_amdgcn_permlane16_swap(0u, 1u, false, false)[0];
+}
+
+// The other tile's maximum, from the lane of the neighbouring row: after a
+// row-pair swap of r with itself a lane holds its own value and its
+// neighbour's, in an order that does not matter (equal values are the same).
+__device__ __forceinline__ float other_tile_max(float r) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(r), __float_as_uint(r), false, false);
+  return s[0] == __float_as_uint(r) ? __uint_as_float(s[1]) : __uint_as_float(s[0]);
+}
+
 // FP8: the pools hold E4M3 bytes; the loader widens them exactly to bf16 on
 // their way into LDS (waves 0-3 load K, waves 4-7 V, 16 elements per lane), so
 // everything after the LDS tiles is the bf16 path.  k_scale is already in
@@ -147,6 +183,15 @@ prefill_lds_kernel(const PrefillArgs a) {
   const Elem* vc = reinterpret_cast<const Elem*>(a.value_cache);
   const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.query);
   const int ld_row = tid >> 4, ld_chunk = tid & 15;    // loader: 16 lanes per 256 B row (32 rows)
+  static_assert(kPfTiles == 2, "the column maxima pair the two tiles of a wave");
+  // A negative scale is folded into the query: flipping the sign bits of q
+  // negates every score exactly, so the softmax below always works with a
+  // non-negative scale sl2 and a column's largest raw score is its largest
+  // scaled one.  inv_sl2 = 1 / sl2 (+inf for scale 0) turns a reference
+  // maximum into a threshold on raw scores.
+  const bool neg_scale = a.scale_log2 < 0.f;
+  const float sl2 = fabsf(a.scale_log2), inv_sl2 = 1.f / sl2;
+  const int my_tile = tile_of_lane();
 
   while (true) {
     __syncthreads();                                   // everyone has read the previous item
@@ -185,6 +230,9 @@ prefill_lds_kernel(const PrefillArgs a) {
       const int row = f / G, head = f - row * G;
       pos[t] = ctx + row;
       Tile::load_q_col(q[t], qbase + ((int64_t)(qrow0 + row) * Hq + h * G + head) * D, f < f1w);
+      if (neg_scale)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) q[t].q[kk] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
     }
 
     BlockWindow win;
@@ -249,7 +297,11 @@ prefill_lds_kernel(const PrefillArgs a) {
     // osum: the softmax denominators, accumulated by the MFMA against an
     // all-ones A tile (every row of it is the column's sum of the bf16 weights
     // that multiply V), so the VALU does no per-element adds.
+    // mref: each column's reference maximum (log2 units, scaled); mref_own:
+    // that of this lane's own tile (my_tile); thr_own: the raw score above
+    // which that column outgrows its reference by more than the slack.
     float mref[kPfTiles];
+    float mref_own = -INFINITY, thr_own = -INFINITY;
     f32x4 o[kPfTiles][NDT], osum[kPfTiles];
 #pragma unroll
     for (int t = 0; t < kPfTiles; ++t) {
@@ -259,11 +311,13 @@ prefill_lds_kernel(const PrefillArgs a) {
       for (int d = 0; d < NDT; ++d) o[t][d] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Phase A of a chunk: scores of all tiles from the shared K tile, masked
-    // on diagonal chunks, and each column's scaled maximum.
+    // Phase A of a chunk: scores of all tiles from the shared K tile and the
+    // column maximum of this lane's tile.  Off the diagonal the scores stay
+    // raw (the scale goes into the exponent's fma); on diagonal chunks they
+    // are scaled first and the masked ones set to -inf, so a masked key gets
+    // weight 0 whatever the scale (also 0: -inf * 0 would be NaN).
     f32x4 sc[kPfTiles][2];
-    float cmx[kPfTiles];
-    auto scores = [&](int b, int ch, auto diag_tag) {
+    auto scores = [&](int b, int ch, auto diag_tag) -> float {
       constexpr bool DIAG = decltype(diag_tag)::value;
       const uint8_t* Kt = kbuf[b];
       u32x4 kop[2][4];
@@ -274,6 +328,7 @@ prefill_lds_kernel(const PrefillArgs a) {
           const int row = 16 * u + col;
           kop[u][kk] = *reinterpret_cast<const u32x4*>(Kt + row * RB + (((4 * kk + c) ^ (row & 15)) << 4));
         }
+      float lmax[kPfTiles];
 #pragma unroll
       for (int t = 0; t < kPfTiles; ++t) {
 #pragma unroll
@@ -289,11 +344,13 @@ prefill_lds_kernel(const PrefillArgs a) {
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            if constexpr (DIAG) sc[t][u][r] = (ch * 32 + 16 * u + 4 * c + r <= pos[t]) ? sc[t][u][r] : -INFINITY;
+            if constexpr (DIAG)
+              sc[t][u][r] = (ch * 32 + 16 * u + 4 * c + r <= pos[t]) ? sc[t][u][r] * sl2 : -INFINITY;
             cmax = fmaxf(cmax, sc[t][u][r]);
           }
-        cmx[t] = wave_max_across_rows_swap(cmax) * a.scale_log2;
+        lmax[t] = cmax;
       }
+      return pair_tile_max(lmax[0], lmax[1]);
     };
     // Phase B: weights against the current reference maxima, then O^T += V^T P^T.
     // Row i of O^T tile dt is dim i + 16 dt; k-slot 4u + r is token 16u + 4c + r,
@@ -305,7 +362,7 @@ prefill_lds_kernel(const PrefillArgs a) {
     // dim 16 dt + i of tokens 16u + 4c .. + 3: k-slots 4u .. 4u + 3.
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-    auto accumulate = [&](int b) {
+    auto accumulate = [&](int b, float mul) {
       const uint8_t* vlane = vbuf[b] + (4 * c + (col >> 2)) * VR + 8 * (col & 3);
       bf16x8 pb[kPfTiles];
       constexpr uint32_t kOnes = 0x3F803F80u;           // two bf16 1.0
@@ -315,7 +372,7 @@ prefill_lds_kernel(const PrefillArgs a) {
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            pb[t][4 * u + r] = (__bf16)fast_exp2(fmaf(sc[t][u][r], a.scale_log2, -mref[t]));
+            pb[t][4 * u + r] = (__bf16)fast_exp2(fmaf(sc[t][u][r], mul, -mref[t]));
         osum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u32x4{kOnes, kOnes, kOnes, kOnes}),
                                                          pb[t], osum[t], 0, 0, 0);
       }
@@ -330,6 +387,31 @@ prefill_lds_kernel(const PrefillArgs a) {
         for (int t = 0; t < kPfTiles; ++t)
           o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb[t], o[t][dt], 0, 0, 0);
       }
+    };
+
+    // Scores, rescale if a column's maximum outgrew its reference by more
+    // than the slack (always on the first chunk; a rare, wave-uniform
+    // branch), then PV.  The test is on raw scores against thr_own off the
+    // diagonal and on scaled ones against mref_own on it.
+    auto chunk = [&](int b, int ch, bool diag) {
+      const float m = diag ? scores(b, ch, std::true_type{}) : scores(b, ch, std::false_type{});
+      if (__any(m > (diag ? mref_own + kRescaleSlack : thr_own))) {
+        const float m_other = other_tile_max(m);
+#pragma unroll
+        for (int t = 0; t < kPfTiles; ++t) {
+          const float v = t == my_tile ? m : m_other;
+          const float cmx = diag ? v : v * sl2;
+          const bool nt = diag ? v > mref[t] + kRescaleSlack : v > (mref[t] + kRescaleSlack) * inv_sl2;
+          const float alpha = nt ? fast_exp2(mref[t] - cmx) : 1.f;       // 0 on the first chunk
+          mref[t] = nt ? cmx : mref[t];
+          osum[t] *= alpha;
+#pragma unroll
+          for (int d = 0; d < NDT; ++d) o[t][d] *= alpha;
+        }
+        mref_own = my_tile ? mref[1] : mref[0];
+        thr_own = (mref_own + kRescaleSlack) * inv_sl2;
+      }
+      accumulate(b, diag ? 1.f : sl2);
     };
 
     const int nch = (p_max + 32) / 32;
@@ -348,23 +430,7 @@ prefill_lds_kernel(const PrefillArgs a) {
     auto step = [&](int ch, auto par_tag) {
       constexpr int P = decltype(par_tag)::value;
       if (has && ch * 32 <= p_max_w) {
-        if (ch * 32 + 31 > p_min_w) scores(P, ch, std::true_type{});
-        else scores(P, ch, std::false_type{});
-        bool need = false;
-#pragma unroll
-        for (int t = 0; t < kPfTiles; ++t) need |= cmx[t] > mref[t] + kRescaleSlack;
-        if (__any(need)) {
-#pragma unroll
-          for (int t = 0; t < kPfTiles; ++t) {
-            const bool nt = cmx[t] > mref[t] + kRescaleSlack;
-            const float alpha = nt ? fast_exp2(mref[t] - cmx[t]) : 1.f;   // 0 on the first chunk
-            mref[t] = nt ? cmx[t] : mref[t];
-            osum[t] *= alpha;
-#pragma unroll
-            for (int d = 0; d < NDT; ++d) o[t][d] *= alpha;
-          }
-        }
-        accumulate(P);
+        chunk(P, ch, ch * 32 + 31 > p_min_w);
       }
       // Past the last chunk the loads and stores are clamped and unused; the
       // buffer stored into was last read before the previous barrier.

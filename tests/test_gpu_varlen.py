@@ -64,6 +64,17 @@ def test_reduced_shapes(name, seed, dev):
     _check(W.generate(SMALL[name], seed=seed), dev, name)
 
 
+@pytest.mark.parametrize("scale", [-1.0 / np.sqrt(128.0), 0.0, 0.75])
+@pytest.mark.parametrize("name", ["gqa8-bs16", "gqa8-long-chunk", "gqa4-bs32"])
+def test_any_finite_scale(name, scale, dev):
+    """The API takes any finite scale.  A negative one flips which key is
+    largest, zero gives uniform weights (the mean of the visible values) and
+    a large one makes the running maxima move often; all must match."""
+    wl = W.generate(SMALL[name], seed=31)
+    wl.scale = float(scale)
+    _check(wl, dev, "%s scale %g" % (name, scale))
+
+
 def test_mixed_batch_of_the_page_example(dev, golden):
     """Two decode rows plus prefills of 50 and 30 rows: 82 rows, 4 requests."""
     ex = golden["mixed_batch"]
