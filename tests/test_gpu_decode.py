@@ -19,7 +19,7 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _check_full(wl, dev, label):
+def _check_full(wl, dev, label, rel_factor=1.0):
     log("[%s] seed %d: B=%d T=%d NB=%d maxL=%d" % (label, wl.seed, wl.num_seqs, wl.num_tokens, wl.num_blocks,
                                                    wl.max_seq_len))
     t = upload(wl, dev)
@@ -27,7 +27,7 @@ def _check_full(wl, dev, label):
     r_slots, r_kc, r_vc, r_out = oracle_step(wl)
     assert np.array_equal(slots.cpu().numpy(), r_slots), "slot mapping differs"
     assert same_bits(t["key_cache"], r_kc) and same_bits(t["value_cache"], r_vc), "cache contents differ"
-    assert_attn_close(out, r_out, wl.spec.dtype, label)
+    assert_attn_close(out, r_out, wl.spec.dtype, label, rel_factor)
     return t, out
 
 
@@ -87,6 +87,27 @@ def test_lengths_at_chunk_edges(dev):
     lens = (1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 1000)
     spec = W.reduced(3, num_decode=len(lens), decode_len=("fixed", lens))
     _check_full(W.generate(spec, seed=9), dev, "edges")
+
+
+def test_maximum_sequence_count(dev):
+    """8192 sequences, the most one call takes (the split kernel keeps one
+    prefix-sum entry per sequence in LDS): lengths 1 .. 48, GQA 8 / 2, D 64."""
+    spec = W.reduced(3, num_decode=8192, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                     decode_len=("uniform", 1, 48))
+    _check_full(W.generate(spec, seed=41), dev, "8192 sequences")
+
+
+@pytest.mark.parametrize("scale", [-1.0 / np.sqrt(128.0), 0.0, 0.75])
+@pytest.mark.parametrize("name", ["gqa8-bs16", "gqa16-d64", "f32-d128"])
+def test_any_finite_scale(name, scale, dev):
+    """Any finite scale: negative (the smallest score wins), zero (the mean
+    of the visible values, masked tail slots still excluded) and large.  The
+    exponent's rounding error grows with the scores, so the relative-L2
+    self-check grows with |scale| * sqrt(D) (1 at the usual 1/sqrt(D)); the
+    max-abs bar does not move."""
+    wl = W.generate(SMALL[name], seed=33)
+    wl.scale = float(scale)
+    _check_full(wl, dev, "%s scale %g" % (name, scale), max(1.0, abs(scale) * np.sqrt(wl.spec.head_dim)))
 
 
 def test_zero_length_sequence_gives_zero_row(dev):
