@@ -4,9 +4,10 @@
 
 A step is one decode iteration of the 128-sequence GQA workload (64 query /
 8 KV heads, head_dim 128, bf16 KV, 16-token blocks, lognormal lengths with
-median 1500 clipped to [16, 8192]): slot mapping and cache write of the
-step's new tokens (pkv_write_new_tokens, one kernel) -> paged decode
-attention (split kernel + merge kernel).
+median 1500 clipped to [16, 8192]): one pkv_decode_step call -- the split
+kernel, which also maps and writes the step's new tokens into their slots,
+then the merge kernel (--two-call: pkv_write_new_tokens, then
+pkv_paged_attention_decode).
 Inputs are resident in HBM before timing starts.  Prints one JSON line.
 --config N runs another seeded workload the same way (1-4 decode; 5 is the
 mixed chunked-prefill + decode step, timed through the varlen call, whose
@@ -21,6 +22,10 @@ from HIP events the library records around that kernel on its stream during a
 second pass of the same K steps (the events are kept out of the first, timed
 pass because each record adds a few microseconds of queue serialisation).
 cpu_baseline = the float64 oracle on a bounded sample of the same batch.
+cold_step_ms = the same step timed alone after 1 GiB of scratch was written
+(no cache holds the previous step's data); hbm_stream_read_GBps = the
+library's plain streaming read over 4 GiB (pkv_stream_read), the read rate
+this part reaches in practice.
 """
 from __future__ import annotations
 
@@ -446,6 +451,33 @@ def main() -> int:
     torch.cuda.synchronize()
     kern_ms = [ops.HipEvent.elapsed_ms(e0, e1) for e0, e1 in evs]
     ms_step = total_ms / args.steps
+    # Region C: each step timed alone after the library's streaming read of
+    # 1 GiB of other data (outside its events, read-only so no dirty lines
+    # are left to write back), so neither the L2s nor the 256 MB last-level
+    # cache hold anything of the previous step.
+    sink = torch.zeros(8192, dtype=torch.int32, device=dev)
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in cold:
+        ops.stream_read(scratch, sink)
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    cold_ms = [e0.elapsed_time(e1) for e0, e1 in cold]
+    del scratch
+    # The same streaming read over 4 GiB: the HBM read rate this part reaches
+    # in practice, next to the 8 TB/s peak.
+    big = torch.ones(1 << 30, dtype=torch.int32, device=dev)
+    ops.stream_read(big, sink)
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for _ in range(10):
+        ops.stream_read(big, sink)
+    r1.record()
+    torch.cuda.synchronize()
+    stream_gbps = 10 * big.numel() * 4 / (r0.elapsed_time(r1) * 1e-3) / 1e9
+    del big
     kv_bytes = wl.kv_bytes_logical() // (2 if fp8 else 1)
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     k_mean = float(np.mean(kern_ms))
@@ -491,6 +523,11 @@ def main() -> int:
         "kv_tokens_per_s": round(float(wl.seq_lens.sum()) / (ms_step * 1e-3), 1),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "cold_step_ms": {"median": round(float(np.median(cold_ms)), 5), "min": round(float(np.min(cold_ms)), 5),
+                         "p90": round(float(np.percentile(cold_ms, 90)), 5),
+                         "value_at_median": round(kv_bytes / (float(np.median(cold_ms)) * 1e-3) / 1e9, 2),
+                         "how": "each step alone, after a streaming read of 1 GiB of other data (caches cold)"},
+        "hbm_stream_read_GBps": round(stream_gbps, 1),
     }
     print(json.dumps(rec), flush=True)
     return 0

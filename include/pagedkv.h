@@ -355,6 +355,20 @@ int pkv_swap_blocks(const void* src_key, const void* src_value, void* dst_key, v
  * (-1 for an out-of-range argument).
  */
 int pkv_set_profile_events(void* start_event, void* stop_event);
+
+/*
+ * pkv_stream_read: enqueue a plain streaming read of `bytes` bytes (a multiple
+ * of 16) at device pointer `buf` (16-byte aligned): the HBM read rate the part
+ * reaches in practice, to quote beside its peak, and a read-only way to push
+ * other data out of the caches before a cold timing.  Not part of the paged
+ * attention method.  sink: device uint32 [sink_len], sink_len a multiple of 4
+ * in [4, 262144]; the read uses sink_len / 4 workgroups and stores the XOR of
+ * the words each wavefront read into one sink entry (so the XOR of the whole
+ * sink is the XOR of the buffer's 32-bit words).  bytes == 0 enqueues nothing.
+ * PKV_EINVAL for null pointers, misalignment or a bad length.
+ */
+int pkv_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t sink_len, void* stream);
+
 int pkv_set_decode_workers(int32_t workers);
 int pkv_set_waves_per_cu(int32_t waves);
 int pkv_set_decode_segment_cost(int32_t chunks);

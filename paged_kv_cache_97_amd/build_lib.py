@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 SOURCES = ["api.hip", "cache_kernels.hip", "decode_kernels.hip", "varlen_kernels.hip", "prefill_lds_kernels.hip",
-           "block_kernels.hip", "scheduler.cpp"]
+           "block_kernels.hip", "measure_kernels.hip", "scheduler.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

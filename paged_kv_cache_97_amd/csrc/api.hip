@@ -121,6 +121,17 @@ int pkv_set_profile_events(void* start_event, void* stop_event) {
   return ok();
 }
 
+int pkv_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t sink_len, void* stream) {
+  if (bytes == 0) return ok();
+  if (!buf || !sink) return fail(PKV_EINVAL, "null pointer");
+  if (!aligned16(buf) || bytes % 16) return fail(PKV_EINVAL, "buffer must be 16-byte aligned and a multiple of 16 bytes");
+  if (sink_len < 4 || sink_len > 262144 || sink_len % 4)
+    return fail(PKV_EINVAL, "sink_len %d must be a multiple of 4 in [4, 262144]", sink_len);
+  const hipError_t e = pkv::launch_stream_read(buf, (int64_t)bytes, sink, sink_len / 4,
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "stream read launch");
+}
+
 int pkv_set_decode_segment_cost(int32_t chunks) {
   if (chunks < 0 || chunks > 64) return -1;
   return g_seg_chunks.exchange(chunks);

@@ -133,4 +133,9 @@ hipError_t launch_block_copy(const void* src0, void* dst0, const void* src1, voi
                              int num_pairs, int64_t src_blocks, int64_t dst_blocks, int64_t block_bytes,
                              hipStream_t stream);
 
+// Streaming read of bytes (a multiple of 16) from buf with `blocks`
+// workgroups of 256 threads; sink receives one XOR word per wavefront
+// (blocks * 4 words).
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
+
 }  // namespace pkv

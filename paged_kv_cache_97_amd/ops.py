@@ -64,6 +64,7 @@ _SIGNATURES = {
     "pkv_copy_blocks": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp]),
     "pkv_swap_blocks": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_vp]),
     "pkv_set_profile_events": (_c_i32, [_c_vp, _c_vp]),
+    "pkv_stream_read": (_c_i32, [_c_vp, _c_sz, _c_vp, _c_i32, _c_vp]),
     "pkv_set_decode_workers": (_c_i32, [_c_i32]),
     "pkv_set_waves_per_cu": (_c_i32, [_c_i32]),
     "pkv_set_decode_segment_cost": (_c_i32, [_c_i32]),
@@ -534,3 +535,12 @@ class HipEvent:
 def set_profile_events(start: Optional[HipEvent], stop: Optional[HipEvent]) -> None:
     _check(lib().pkv_set_profile_events(start.handle if start else None, stop.handle if stop else None),
            "set_profile_events")
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Enqueue a plain streaming read of buf's bytes (a measuring stick for the
+    HBM read rate, or a read-only cache flush); sink (int32 holding the uint32
+    words, length a multiple of 4) receives one XOR word per wavefront."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().pkv_stream_read(_dev(buf, "buf"), nbytes, _dev(sink, "sink", torch.int32, 1), sink.numel(),
+                                 _stream(buf)), "stream_read")

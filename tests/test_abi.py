@@ -161,3 +161,13 @@ def test_decode_step_validation_runs_before_any_launch(fp8, kw, code):
     assert _step(lib, fp8, **kw) == code
     if code:
         assert lib.pkv_last_error()
+
+
+def test_stream_read_validation():
+    lib = ops.lib()
+    assert lib.pkv_stream_read(None, 0, None, 0, None) == 0                       # nothing to read
+    assert lib.pkv_stream_read(None, 16, ctypes.c_void_p(1 << 20), 4, None) == 1  # null buffer
+    assert lib.pkv_stream_read(ctypes.c_void_p(1 << 20), 24, ctypes.c_void_p(1 << 20), 4, None) == 1
+    assert lib.pkv_stream_read(ctypes.c_void_p((1 << 20) + 8), 32, ctypes.c_void_p(1 << 20), 4, None) == 1
+    for bad in (0, 6, 262148):
+        assert lib.pkv_stream_read(ctypes.c_void_p(1 << 20), 32, ctypes.c_void_p(1 << 20), bad, None) == 1
