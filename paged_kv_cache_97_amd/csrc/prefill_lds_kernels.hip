@@ -3,15 +3,17 @@
 // Same computation as prefill_kernel (gaoleia.github.io "PagedAttention 和
 // Continuous Batching" §2.4-§2.5: a chunk of q rows after c cached tokens,
 // row i attends keys 0 .. c + i), organised for the MFMA rate of gfx950:
-//  * a workgroup of 8 waves (two per SIMD, so one wave's MFMAs overlap the
-//    other's softmax) owns an item of 256 (row, head) columns of one
-//    (sequence, KV head); each 32-token K/V chunk is loaded once per
-//    workgroup into double-buffered LDS and read by all 8 waves, each
-//    computing 2 tiles of 16 columns.  K is kept token-major (XOR-swizzled
-//    256 B rows); V is stored transposed (dim-major, 72 B rows of 32 tokens +
-//    pad) by a loader whose consecutive lanes hold consecutive tokens, so the
-//    transposed stores are contiguous and each lane reads its PV operand --
-//    8 tokens of one dim -- with two 8-byte reads, no in-register transpose;
+//  * a workgroup of 8 waves (two per SIMD) owns an item of 256 (row, head)
+//    columns of one (sequence, KV head); each 32-token K/V chunk is loaded
+//    once per workgroup into LDS (K in two buffers, V in three) and read by
+//    all 8 waves, each computing 2 tiles of 16 columns.  K is kept
+//    token-major in XOR-swizzled 256 B rows; V token-major in 288 B rows, and
+//    each lane reads its PV operand -- 8 tokens of one dim -- with two
+//    transposing 8-byte LDS reads (ds_read_b64_tr_b16);
+//  * the two waves of a SIMD are staggered: waves 0-3 take chunk n's scores,
+//    weights and PV between two barriers, waves 4-7 the weights and PV of
+//    chunk n - 1 and then chunk n's scores, so one wave's softmax VALU work
+//    meets the other's MFMA work;
 //  * the O^T accumulators stay in the accumulation registers: the softmax
 //    reference maximum is only moved when a column's maximum grows by more
 //    than 2^8 (the rescale is exact; weights up to 256 are fine in bf16/fp32),
@@ -166,7 +168,7 @@ prefill_lds_kernel(const PrefillArgs a) {
   // per-dim-tile addresses are immediate offsets.
   constexpr int VR = 288;
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][32 * RB];       // [buffer][32 token rows]
-  __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][32 * VR];       // [buffer][32 token rows]
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf[3][32 * VR];       // [buffer][32 token rows]
   __shared__ int s_item;
   // wave is read through readfirstlane so the compiler knows every per-wave
   // decision below is uniform: scalar branches, no exec-masked loop exits.
@@ -268,7 +270,7 @@ prefill_lds_kernel(const PrefillArgs a) {
         R[1] = ld16(addr(vc, ld_row, 8 * ld_chunk));
       }
     };
-    auto store_chunk = [&](int ch, int b, const u32x4* R) {
+    auto store_chunk = [&](int ch, int kb, int vb, const u32x4* R) {
       if constexpr (FP8) {
         const int row = (tid >> 3) & 31, p = tid & 7;
         const bool vpast = !kthr && ch * 32 + row > p_max;
@@ -280,16 +282,16 @@ prefill_lds_kernel(const PrefillArgs a) {
           d[2 * q4 + 1] = fp8x2_to_bf16x2(x[q4], true);
         }
         if (kthr) {
-          *reinterpret_cast<u32x4*>(&kbuf[b][row * RB + (((2 * p) ^ (row & 15)) << 4)]) = u32x4{d[0], d[1], d[2], d[3]};
-          *reinterpret_cast<u32x4*>(&kbuf[b][row * RB + (((2 * p + 1) ^ (row & 15)) << 4)]) =
+          *reinterpret_cast<u32x4*>(&kbuf[kb][row * RB + (((2 * p) ^ (row & 15)) << 4)]) = u32x4{d[0], d[1], d[2], d[3]};
+          *reinterpret_cast<u32x4*>(&kbuf[kb][row * RB + (((2 * p + 1) ^ (row & 15)) << 4)]) =
               u32x4{d[4], d[5], d[6], d[7]};
         } else {
-          *reinterpret_cast<u32x4*>(&vbuf[b][row * VR + 32 * p]) = u32x4{d[0], d[1], d[2], d[3]};
-          *reinterpret_cast<u32x4*>(&vbuf[b][row * VR + 32 * p + 16]) = u32x4{d[4], d[5], d[6], d[7]};
+          *reinterpret_cast<u32x4*>(&vbuf[vb][row * VR + 32 * p]) = u32x4{d[0], d[1], d[2], d[3]};
+          *reinterpret_cast<u32x4*>(&vbuf[vb][row * VR + 32 * p + 16]) = u32x4{d[4], d[5], d[6], d[7]};
         }
       } else {
-        *reinterpret_cast<u32x4*>(&kbuf[b][ld_row * RB + ((ld_chunk ^ (ld_row & 15)) << 4)]) = R[0];
-        *reinterpret_cast<u32x4*>(&vbuf[b][ld_row * VR + 16 * ld_chunk]) =
+        *reinterpret_cast<u32x4*>(&kbuf[kb][ld_row * RB + ((ld_chunk ^ (ld_row & 15)) << 4)]) = R[0];
+        *reinterpret_cast<u32x4*>(&vbuf[vb][ld_row * VR + 16 * ld_chunk]) =
             ch * 32 + ld_row > p_max ? u32x4{0, 0, 0, 0} : R[1];
       }
     };
@@ -389,12 +391,12 @@ prefill_lds_kernel(const PrefillArgs a) {
       }
     };
 
-    // Scores, rescale if a column's maximum outgrew its reference by more
-    // than the slack (always on the first chunk; a rare, wave-uniform
-    // branch), then PV.  The test is on raw scores against thr_own off the
-    // diagonal and on scaled ones against mref_own on it.
-    auto chunk = [&](int b, int ch, bool diag) {
-      const float m = diag ? scores(b, ch, std::true_type{}) : scores(b, ch, std::false_type{});
+    // If a column's maximum m (scaled on the diagonal, raw off it) outgrew
+    // its reference by more than the slack (always on the first chunk; a
+    // rare, wave-uniform branch) rescale that column's accumulators.  The test
+    // is on raw scores against thr_own off the diagonal and on scaled ones
+    // against mref_own on it.
+    auto rescale_if_needed = [&](float m, bool diag) {
       if (__any(m > (diag ? mref_own + kRescaleSlack : thr_own))) {
         const float m_other = other_tile_max(m);
 #pragma unroll
@@ -411,39 +413,71 @@ prefill_lds_kernel(const PrefillArgs a) {
         mref_own = my_tile ? mref[1] : mref[0];
         thr_own = (mref_own + kRescaleSlack) * inv_sl2;
       }
-      accumulate(b, diag ? 1.f : sl2);
     };
 
     const int nch = (p_max + 32) / 32;
     load_chunk(0, S[0]);
     load_chunk(1, S[1]);
-    store_chunk(0, 0, S[0]);
+    store_chunk(0, 0, 0, S[0]);
     load_chunk(2, S[0]);
     __syncthreads();
-    // One chunk: scores from LDS buffer P (= ch & 1); when a column's maximum
-    // outgrows its reference by more than the slack (always on the first
-    // chunk) the wave rescales first (a rare, wave-uniform branch); then PV,
-    // chunk ch + 1 (register set 1 - P, loaded two steps ago) into LDS buffer
-    // 1 - P, the same set reloaded at once with chunk ch + 3, barrier.  A set
-    // is never idle between its store and its reload, and its loads have two
-    // steps to land.
-    auto step = [&](int ch, auto par_tag) {
+    // Staggered waves.  Both waves of a SIMD (w and w + 4) work between the
+    // same two barriers, but in different orders, so that one wave's softmax
+    // VALU work runs while the other's products keep the matrix core busy:
+    //   waves 0-3, step n:  scores(n) -> weights and PV of n
+    //   waves 4-7, step n:  weights and PV of n - 1 -> scores(n)
+    // (a lagging wave keeps chunk n's scores in registers across the barrier).
+    // Step n reads K chunk n (buffer n & 1) and V chunks n and n - 1 (buffers
+    // n % 3 and (n - 1) % 3), stores chunk n + 1 (register set 1 - P, loaded
+    // two steps ago) into K buffer 1 - P and V buffer (n + 1) % 3 -- both last
+    // read before the previous barrier -- reloads that set with chunk n + 3,
+    // then the barrier.  The loop runs one step past the last chunk for the
+    // lagging waves' last PV.
+    float m_lag = 0.f;                                   // lagging waves: the held chunk's maximum
+    bool diag_lag = false;
+    int v_prev = 2, v_cur = 0, v_next = 1;               // (n - 1) % 3, n % 3, (n + 1) % 3
+    auto step = [&](int n, auto par_tag, auto lag_tag) {
       constexpr int P = decltype(par_tag)::value;
-      if (has && ch * 32 <= p_max_w) {
-        chunk(P, ch, ch * 32 + 31 > p_min_w);
+      constexpr bool LAG = decltype(lag_tag)::value;
+      const bool have_n = has && n < nch && n * 32 <= p_max_w;
+      if constexpr (!LAG) {
+        if (have_n) {
+          const bool diag = n * 32 + 31 > p_min_w;
+          const float m = diag ? scores(P, n, std::true_type{}) : scores(P, n, std::false_type{});
+          rescale_if_needed(m, diag);
+          accumulate(v_cur, diag ? 1.f : sl2);
+        }
+      } else {
+        if (has && n > 0 && (n - 1) * 32 <= p_max_w) {
+          rescale_if_needed(m_lag, diag_lag);
+          accumulate(v_prev, diag_lag ? 1.f : sl2);
+        }
+        if (have_n) {
+          diag_lag = n * 32 + 31 > p_min_w;
+          m_lag = diag_lag ? scores(P, n, std::true_type{}) : scores(P, n, std::false_type{});
+        }
       }
-      // Past the last chunk the loads and stores are clamped and unused; the
-      // buffer stored into was last read before the previous barrier.
-      store_chunk(ch + 1, 1 - P, S[1 - P]);
-      load_chunk(ch + 3, S[1 - P]);
+      // Past the last chunk the loads and stores are clamped and unused.
+      store_chunk(n + 1, 1 - P, v_next, S[1 - P]);
+      load_chunk(n + 3, S[1 - P]);
+      v_prev = v_cur;
+      v_cur = v_next;
+      v_next = v_next == 2 ? 0 : v_next + 1;
       __syncthreads();
     };
-    // Even and odd chunks alternate in straight-line code (an odd step past
-    // the last chunk computes nothing), so the compiler's wait counting sees
-    // which register set is older and waits only for it.
-    for (int ch = 0; ch < nch; ch += 2) {
-      step(ch, std::integral_constant<int, 0>{});
-      step(ch + 1, std::integral_constant<int, 1>{});
+    // Even and odd steps alternate in straight-line code, so the compiler's
+    // wait counting sees which register set is older and waits only for it.
+    // One loop per role (the same barriers in the same number).
+    if (wave >= kPfWaves / 2) {
+      for (int n = 0; n <= nch; n += 2) {
+        step(n, std::integral_constant<int, 0>{}, std::true_type{});
+        step(n + 1, std::integral_constant<int, 1>{}, std::true_type{});
+      }
+    } else {
+      for (int n = 0; n <= nch; n += 2) {
+        step(n, std::integral_constant<int, 0>{}, std::false_type{});
+        step(n + 1, std::integral_constant<int, 1>{}, std::false_type{});
+      }
     }
 
 #pragma unroll
