@@ -51,12 +51,17 @@ int current_cus() {
   return cus;
 }
 
-int decode_workers() {
+// Wavefronts sharing a decode split: the forced count if one is set, else
+// waves-per-CU times the compute units, but never more than max_chunks, an
+// upper bound of the chunks the launch can hold (workers beyond the chunk
+// count would only add empty parts for the merge to step over).
+int decode_workers(int64_t max_chunks = INT64_MAX) {
   const int forced = g_workers_override.load();
   if (forced > 0) return forced;
   int cus = current_cus();
   if (cus <= 0) cus = 256;
-  return cus * g_waves_per_cu.load();
+  const int64_t full = (int64_t)cus * g_waves_per_cu.load();
+  return (int)std::max<int64_t>(1, std::min(full, max_chunks));
 }
 
 int check_shape(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -87,12 +92,17 @@ KvFormat plain_format(pkv_dtype dt) { return {dt == PKV_BF16 ? pkv::KvKind::BF16
 // A pool scale must be positive and finite with a finite float32 reciprocal.
 bool good_scale(float s) { return std::isfinite(s) && s > 0.f && std::isfinite(1.0f / s); }
 
-// Upper bound of the chunk count the split sees, times the worker count, must
-// stay far inside int64 (the kernels multiply the two).
-bool split_fits(int64_t num_seqs, int64_t pairs_per_seq, int64_t max_tokens, int64_t workers) {
-  const int64_t chunks = num_seqs * pairs_per_seq * ((max_tokens + 31) / 32 + g_seg_chunks.load());
-  return chunks < (int64_t(1) << 40) && workers <= 65536;
+// Upper bound of the chunks (real and virtual) a decode split can see:
+// sequences x (KV head, head tile) pairs x chunks per pair, computed in 128
+// bits and saturated so that no argument values overflow it.
+int64_t chunk_bound(int64_t num_seqs, int64_t pairs_per_seq, int64_t max_tokens, int seg_chunks) {
+  const __int128 n = (__int128)num_seqs * pairs_per_seq * ((max_tokens + 31) / 32 + seg_chunks);
+  return n > (__int128)INT64_MAX ? INT64_MAX : (int64_t)n;
 }
+
+// The chunk count times the worker count must stay far inside int64 (the
+// kernels multiply the two).
+bool split_fits(int64_t chunks, int64_t workers) { return chunks < (int64_t(1) << 40) && workers <= 65536; }
 
 }  // namespace
 
@@ -346,10 +356,12 @@ static int run_decode(float* out, const void* query, const void* key_cache, cons
                       float scale, KvFormat fmt, void* workspace, size_t workspace_bytes,
                       hipStream_t stream, const void* new_k = nullptr, const void* new_v = nullptr) {
   const int group = num_q_heads / num_kv_heads;
-  const int workers = decode_workers();
   const int head_tiles = (group + 15) / 16;
-  if (!split_fits(num_seqs, (int64_t)num_kv_heads * head_tiles,
-                  (int64_t)max_blocks_per_seq * block_size, workers))
+  const int seg_chunks = g_seg_chunks.load();
+  const int64_t max_chunks = chunk_bound(num_seqs, (int64_t)num_kv_heads * head_tiles,
+                                         (int64_t)max_blocks_per_seq * block_size, seg_chunks);
+  const int workers = decode_workers(max_chunks);
+  if (!split_fits(max_chunks, workers))
     return fail(PKV_EUNSUPPORTED, "problem too large for the split arithmetic");
   const size_t need = pkv::decode_workspace_bytes(num_seqs, num_kv_heads, group, head_dim, workers);
   if (!workspace || workspace_bytes < need)
@@ -374,7 +386,7 @@ static int run_decode(float* out, const void* query, const void* key_cache, cons
   a.scale_log2 = scale * fmt.k_scale * 1.4426950408889634f;
   a.v_scale = fmt.v_scale;
   a.workers = workers;
-  a.seg_chunks = g_seg_chunks.load();
+  a.seg_chunks = seg_chunks;
   a.new_k = new_k;
   a.new_v = new_v;
   a.k_inv = fmt.kind == pkv::KvKind::FP8 ? 1.0f / fmt.k_scale : 1.0f;

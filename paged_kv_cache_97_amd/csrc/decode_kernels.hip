@@ -339,17 +339,20 @@ __global__ void __launch_bounds__(256) decode_reduce_kernel(const DecodeArgs a) 
   const int i0 = (int)(((first + 1) * W - 1) / total);
   const int i1 = (int)(((last + 1) * W - 1) / total);
   if (i0 == i1) return;
-  // Workers between i0 and i1 with an empty range (possible when there are
-  // fewer chunks than workers) wrote nothing.
-  auto empty = [&](int k) { return total * k / W == total * (k + 1) / W; };
+  // With at least as many chunks as workers every worker in [i0, i1] holds a
+  // chunk of the pair.  With fewer, each worker holds at most one chunk and
+  // some hold none: then the parts are the owners of the pair's chunks, one
+  // per chunk, found without walking the empty workers in between.
+  const bool sparse = total < W;
+  const int n_parts = sparse ? (int)(last - first + 1) : i1 - i0 + 1;
   for (int i = threadIdx.x; i < cols * Q4; i += 256) {
     const int col = i / Q4, d4 = i - col * Q4;
     // one pass with a running maximum: rescale what has been merged so far
     float M = -INFINITY, Z = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-    for (int k = i0; k <= i1; ++k) {
-      if (empty(k)) continue;
+    for (int j = 0; j < n_parts; ++j) {
+      const int k = sparse ? (int)(((first + j + 1) * W - 1) / total) : i0 + j;
       const int64_t p = ((int64_t)pair + k) * a.tile_cols + col;
       const float mk = a.part_ml[2 * p], lk = a.part_ml[2 * p + 1];
       const f32x4 ok = *reinterpret_cast<const f32x4*>(a.part_o + p * D + 4 * d4);
