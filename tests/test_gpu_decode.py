@@ -89,6 +89,23 @@ def test_lengths_at_chunk_edges(dev):
     _check_full(W.generate(spec, seed=9), dev, "edges")
 
 
+@pytest.mark.parametrize("lens", [(64, 64, 64), (40, 40), (48, 20), (1,), (96, 96, 33, 96)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_default_workers_fill_the_tables(lens, dtype, dev):
+    """At the default worker count a small batch gets no more waves than its
+    block tables can hold chunks.  Lengths that fill the tables give exactly
+    one chunk per wave (every wave holds a part of its pair); a few shorter
+    rows leave some waves without a chunk, and the merge finds each pair's
+    parts through the owners of its chunks."""
+    prev = ops.set_decode_workers(0)
+    try:
+        spec = W.reduced(3, dtype=dtype, num_decode=len(lens), num_q_heads=8, num_kv_heads=2,
+                         decode_len=("fixed", lens))
+        _check_full(W.generate(spec, seed=33), dev, "default workers %s %s" % (dtype, lens))
+    finally:
+        ops.set_decode_workers(prev)
+
+
 def test_maximum_sequence_count(dev):
     """8192 sequences, the most one call takes (the split kernel keeps one
     prefix-sum entry per sequence in LDS): lengths 1 .. 48, GQA 8 / 2, D 64."""
