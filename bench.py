@@ -224,6 +224,12 @@ def bench_blocks(args) -> int:
     ms_copy = timed(lambda: ops.copy_blocks(kc, vc, cow), args.steps)
     ms_out = timed(lambda: ops.swap_blocks(kc, vc, hk, hv, out_map), max(2, args.steps // 10))
     ms_in = timed(lambda: ops.swap_blocks(hk, hv, kc, vc, in_map), max(2, args.steps // 10))
+    # context: torch's own device-to-device copy of the same volume in one
+    # contiguous piece (no block gather)
+    ref_src = torch.empty(moved // 2, dtype=torch.int16, device=dev).fill_(1)
+    ref_dst = torch.empty_like(ref_src)
+    ms_ref = timed(lambda: ref_dst.copy_(ref_src), args.steps)
+    del ref_src, ref_dst
     print("bench: copy %.4f ms, swap-out %.4f ms, swap-in %.4f ms (%d pairs of 2 x %d B)" % (
         ms_copy, ms_out, ms_in, pairs, blk), file=sys.stderr, flush=True)
     copy_gbs = 2 * moved / (ms_copy * 1e-3) / 1e9
@@ -239,6 +245,7 @@ def bench_blocks(args) -> int:
         "swap_out_gbs": round(moved / (ms_out * 1e-3) / 1e9, 2),
         "swap_in_gbs": round(moved / (ms_in * 1e-3) / 1e9, 2),
         "swap_out_ms": round(ms_out, 4), "swap_in_ms": round(ms_in, 4),
+        "device_copy_gbs": round(2 * moved / (ms_ref * 1e-3) / 1e9, 2),
     }
     print(json.dumps(rec), flush=True)
     return 0

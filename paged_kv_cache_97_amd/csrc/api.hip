@@ -286,7 +286,7 @@ int pkv_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_map
   if (!key_cache || !value_cache || !block_mapping) return fail(PKV_EINVAL, "null pointer");
   if (!aligned16(key_cache) || !aligned16(value_cache)) return fail(PKV_EINVAL, "pools must be 16-byte aligned");
   hipError_t e = pkv::launch_block_copy(key_cache, key_cache, value_cache, value_cache, block_mapping, num_pairs,
-                                        num_blocks, num_blocks, block_bytes, static_cast<hipStream_t>(stream));
+                                        num_blocks, num_blocks, block_bytes, true, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "copy_blocks launch");
 }
 
@@ -337,7 +337,7 @@ int pkv_swap_blocks(const void* src_key, const void* src_value, void* dst_key, v
     return PKV_EINVAL;
   hipError_t e = pkv::launch_block_copy(sk, const_cast<void*>(dk), sv, const_cast<void*>(dv),
                                         static_cast<const int64_t*>(map), num_pairs, src_num_blocks, dst_num_blocks,
-                                        block_bytes, static_cast<hipStream_t>(stream));
+                                        block_bytes, false, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : hip_fail(e, "swap_blocks launch");
 }
 

@@ -20,6 +20,11 @@ namespace pkv {
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;
 
+// NT: non-temporal loads and stores.  Device-to-device copies touch every
+// byte once, and keeping them out of the caches lets the writes stream
+// (+7 % on 4096 pairs of 32 KiB blocks); across PCIe to pinned host memory
+// the plain form is as fast or faster.
+template <bool NT>
 __global__ void __launch_bounds__(kCopyThreads)
 block_copy_kernel(const u32x4* __restrict__ src0, u32x4* __restrict__ dst0, const u32x4* __restrict__ src1,
                   u32x4* __restrict__ dst1, const int64_t* __restrict__ mapping, int64_t src_blocks,
@@ -37,16 +42,21 @@ block_copy_kernel(const u32x4* __restrict__ src0, u32x4* __restrict__ dst0, cons
     for (int u = 0; u < kCopyUnroll; ++u) {
       const int64_t i = base + u * kCopyThreads;
       if (i < block_vecs) {
-        a[u] = src0[so + i];
-        if (src1) b[u] = src1[so + i];
+        a[u] = NT ? __builtin_nontemporal_load(src0 + so + i) : src0[so + i];
+        if (src1) b[u] = NT ? __builtin_nontemporal_load(src1 + so + i) : src1[so + i];
       }
     }
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
       const int64_t i = base + u * kCopyThreads;
       if (i < block_vecs) {
-        dst0[dof + i] = a[u];
-        if (src1) dst1[dof + i] = b[u];
+        if (NT) {
+          __builtin_nontemporal_store(a[u], dst0 + dof + i);
+          if (src1) __builtin_nontemporal_store(b[u], dst1 + dof + i);
+        } else {
+          dst0[dof + i] = a[u];
+          if (src1) dst1[dof + i] = b[u];
+        }
       }
     }
   }
@@ -54,14 +64,18 @@ block_copy_kernel(const u32x4* __restrict__ src0, u32x4* __restrict__ dst0, cons
 
 hipError_t launch_block_copy(const void* src0, void* dst0, const void* src1, void* dst1, const int64_t* mapping,
                              int num_pairs, int64_t src_blocks, int64_t dst_blocks, int64_t block_bytes,
-                             hipStream_t stream) {
+                             bool streaming, hipStream_t stream) {
   const int64_t vecs = block_bytes / 16;
   const int64_t per_wg = (int64_t)kCopyThreads * kCopyUnroll;
   int64_t slices = (vecs + per_wg - 1) / per_wg;
   if (slices > 65535) slices = 65535;
-  hipLaunchKernelGGL(block_copy_kernel, dim3((unsigned)num_pairs, (unsigned)slices), dim3(kCopyThreads), 0, stream,
-                     (const u32x4*)src0, (u32x4*)dst0, (const u32x4*)src1, (u32x4*)dst1, mapping, src_blocks,
-                     dst_blocks, vecs);
+  const dim3 grid((unsigned)num_pairs, (unsigned)slices);
+  if (streaming)
+    hipLaunchKernelGGL(block_copy_kernel<true>, grid, dim3(kCopyThreads), 0, stream, (const u32x4*)src0,
+                       (u32x4*)dst0, (const u32x4*)src1, (u32x4*)dst1, mapping, src_blocks, dst_blocks, vecs);
+  else
+    hipLaunchKernelGGL(block_copy_kernel<false>, grid, dim3(kCopyThreads), 0, stream, (const u32x4*)src0,
+                       (u32x4*)dst0, (const u32x4*)src1, (u32x4*)dst1, mapping, src_blocks, dst_blocks, vecs);
   return hipGetLastError();
 }
 

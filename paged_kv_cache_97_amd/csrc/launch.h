@@ -85,16 +85,6 @@ hipError_t launch_write_tokens_fp8(const int32_t* bt, int num_seqs, int max_bloc
                                    const void* value, void* kc, void* vc, int row_elems, int64_t num_slots,
                                    int64_t* slots, KvKind in_kind, float k_inv, float v_inv, hipStream_t stream);
 
-// Whole-block copies for every (src, dst) pair of mapping (int64 [pairs][2]);
-// src1/dst1 may be null (one pool).  Pairs with an id outside its pool are
-// skipped.
-hipError_t launch_block_copy(const void* src0, void* dst0, const void* src1, void* dst1, const int64_t* mapping,
-                             int num_pairs, int64_t src_blocks, int64_t dst_blocks, int64_t block_bytes,
-                             hipStream_t stream);
-
-}  // namespace pkv
-
-namespace pkv {
 
 // Prefill-chunk rows of a varlen step (sequences with more than one query row).
 struct PrefillArgs {
@@ -128,10 +118,11 @@ hipError_t launch_prefill_lds(const PrefillArgs& a, int block_size, bool fp8, in
 
 // Whole-block copies for every (src, dst) pair of mapping (int64 [pairs][2]);
 // src1/dst1 may be null (one pool).  Pairs with an id outside its pool are
-// skipped.
+// skipped.  streaming: non-temporal loads and stores (copies inside device
+// memory); off for copies to or from pinned host memory.
 hipError_t launch_block_copy(const void* src0, void* dst0, const void* src1, void* dst1, const int64_t* mapping,
                              int num_pairs, int64_t src_blocks, int64_t dst_blocks, int64_t block_bytes,
-                             hipStream_t stream);
+                             bool streaming, hipStream_t stream);
 
 // Streaming read of bytes (a multiple of 16) from buf with `blocks`
 // workgroups of 256 threads; sink receives one XOR word per wavefront
