@@ -77,31 +77,36 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
 constexpr int kTokensPerWg = 8;
 constexpr int kQslLds = 1024;
 
-__global__ void __launch_bounds__(256)
-write_tokens_kernel(const int32_t* __restrict__ block_tables, int num_seqs, int max_blocks,
-                    const int32_t* __restrict__ positions, const int32_t* __restrict__ qsl, int num_tokens,
-                    int block_size, const u32x4* __restrict__ key, const u32x4* __restrict__ value,
-                    u32x4* __restrict__ key_cache, u32x4* __restrict__ value_cache, int row_vecs,
-                    int64_t num_slots, int64_t* __restrict__ slots_out) {
-  __shared__ int qs[kQslLds];
-  __shared__ int64_t s_slot[kTokensPerWg];
+// The slots of tokens t0 .. t0 + kTokensPerWg - 1 into s_slot (and
+// slots_out).  The loads that need no slot -- the owner lanes' positions,
+// query_start_loc for the LDS copy and whatever `prefetch` issues (the first
+// rows of the copy) -- all go out before the first wait, so the chain is two
+// memory round trips: those loads, then the block-table entry.  Ends with a
+// barrier after which s_slot is valid.
+template <typename Prefetch>
+__device__ __forceinline__ void workgroup_slots(const int32_t* __restrict__ block_tables, int num_seqs,
+                                                int max_blocks, const int32_t* __restrict__ positions,
+                                                const int32_t* __restrict__ qsl, int num_tokens, int block_size,
+                                                int64_t* __restrict__ slots_out, int t0, int* qs, int64_t* s_slot,
+                                                Prefetch prefetch) {
   const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * kTokensPerWg;
+  const int t = t0 + tid;
+  const bool owner = tid < kTokensPerWg && t < num_tokens;
+  const int p = owner ? positions[t] : -1;
   const bool staged = num_seqs + 1 <= kQslLds;
+  prefetch();
   if (staged)
     for (int i = tid; i <= num_seqs; i += 256) qs[i] = qsl[i];
   __syncthreads();
   if (tid < kTokensPerWg) {
-    const int t = t0 + tid;
     int64_t slot = -1;
-    if (t < num_tokens) {
+    if (owner) {
       const int32_t* q = staged ? qs : qsl;
       int lo = 0, hi = num_seqs;
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (q[mid] <= t) lo = mid; else hi = mid;
       }
-      const int p = positions[t];
       if (num_seqs > 0 && t < q[lo + 1] && p >= 0) {
         const int lb = p / block_size;
         if (lb < max_blocks) {
@@ -114,43 +119,85 @@ write_tokens_kernel(const int32_t* __restrict__ block_tables, int num_seqs, int 
     s_slot[tid] = slot;
   }
   __syncthreads();
-  const int n = min(kTokensPerWg, num_tokens - t0) * row_vecs;
-  for (int i = tid; i < n; i += 256) {
+}
+
+// Row vectors each lane loads before the slots are known (the rest of the
+// workgroup's rows follow in a plain loop).
+constexpr int kCopyAhead = 4;
+
+__global__ void __launch_bounds__(256)
+write_tokens_kernel(const int32_t* __restrict__ block_tables, int num_seqs, int max_blocks,
+                    const int32_t* __restrict__ positions, const int32_t* __restrict__ qsl, int num_tokens,
+                    int block_size, const u32x4* __restrict__ key, const u32x4* __restrict__ value,
+                    u32x4* __restrict__ key_cache, u32x4* __restrict__ value_cache, int row_vecs,
+                    int64_t num_slots, int64_t* __restrict__ slots_out) {
+  __shared__ int qs[kQslLds];
+  __shared__ int64_t s_slot[kTokensPerWg];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kTokensPerWg;
+  const int n = min(kTokensPerWg, num_tokens - t0) * row_vecs;   // row vectors of this workgroup
+  const int64_t base = (int64_t)t0 * row_vecs;
+  u32x4 ka[kCopyAhead], va[kCopyAhead];
+  workgroup_slots(block_tables, num_seqs, max_blocks, positions, qsl, num_tokens, block_size, slots_out, t0, qs,
+                  s_slot, [&] {
+#pragma unroll
+                    for (int u = 0; u < kCopyAhead; ++u) {
+                      const int i = tid + 256 * u;
+                      if (i < n) {
+                        ka[u] = key[base + i];
+                        va[u] = value[base + i];
+                      }
+                    }
+                  });
+  auto store = [&](int i, const u32x4& k, const u32x4& v) {
     const int tl = i / row_vecs, cvec = i - tl * row_vecs;
     const int64_t slot = s_slot[tl];
-    if (slot < 0 || slot >= num_slots) continue;
-    const int64_t src = (int64_t)(t0 + tl) * row_vecs + cvec;
-    const u32x4 k = key[src];
-    const u32x4 v = value[src];
+    if (slot < 0 || slot >= num_slots) return;
     key_cache[slot * row_vecs + cvec] = k;
     value_cache[slot * row_vecs + cvec] = v;
+  };
+#pragma unroll
+  for (int u = 0; u < kCopyAhead; ++u) {
+    const int i = tid + 256 * u;
+    if (i < n) store(i, ka[u], va[u]);
   }
+  for (int i = tid + 256 * kCopyAhead; i < n; i += 256) store(i, key[base + i], value[base + i]);
 }
 
 // ------------------------------------------------------------------ FP8 stores
-// 16 E4M3 bytes from the 16 input elements of output vector `v` of a row
-// (bf16: two 16-byte input vectors, fp32: four).
+// The 16 input elements of output vector `v` of a row (bf16: two 16-byte
+// input vectors, fp32: four) and their 16 E4M3 bytes.
+template <bool BF16IN>
+struct QuantIn {
+  static constexpr int kVecs = BF16IN ? 2 : 4;   // 16-byte input vectors per 16 output bytes
+  u32x4 x[kVecs];
+  __device__ __forceinline__ void load(const void* in, int64_t v) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(in) + kVecs * v;
+#pragma unroll
+    for (int j = 0; j < kVecs; ++j) x[j] = p[j];
+  }
+  __device__ __forceinline__ u32x4 quant(float inv) const {
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if constexpr (BF16IN) {
+        const u32x4& y = x[w >> 1];
+        const uint32_t lo = y[2 * (w & 1)], hi = y[2 * (w & 1) + 1];
+        out[w] = quant4(bf16_lo(lo), bf16_hi(lo), bf16_lo(hi), bf16_hi(hi), inv);
+      } else {
+        const f32x4 y = __builtin_bit_cast(f32x4, x[w]);
+        out[w] = quant4(y[0], y[1], y[2], y[3], inv);
+      }
+    }
+    return out;
+  }
+};
+
 template <bool BF16IN>
 __device__ __forceinline__ u32x4 quant16(const void* in, int64_t v, float inv) {
-  u32x4 out;
-  if constexpr (BF16IN) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(in) + 2 * v;
-    const u32x4 x0 = p[0], x1 = p[1];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const u32x4& x = w < 2 ? x0 : x1;
-      const uint32_t lo = x[2 * (w & 1)], hi = x[2 * (w & 1) + 1];
-      out[w] = quant4(bf16_lo(lo), bf16_hi(lo), bf16_lo(hi), bf16_hi(hi), inv);
-    }
-  } else {
-    const f32x4* p = reinterpret_cast<const f32x4*>(in) + 4 * v;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const f32x4 x = p[w];
-      out[w] = quant4(x[0], x[1], x[2], x[3], inv);
-    }
-  }
-  return out;
+  QuantIn<BF16IN> x;
+  x.load(in, v);
+  return x.quant(inv);
 }
 
 template <bool BF16IN>
@@ -170,7 +217,12 @@ reshape_and_cache_fp8_kernel(const void* __restrict__ key, const void* __restric
   }
 }
 
-// write_tokens_kernel with quantising stores (same slot computation).
+// write_tokens_kernel with quantising stores (same slot computation).  The
+// raw input vectors of each lane's first kQuantAhead output vectors are
+// loaded before the slots are known.
+constexpr int kQuantAhead = 2;
+
+
 template <bool BF16IN>
 __global__ void __launch_bounds__(256)
 write_tokens_fp8_kernel(const int32_t* __restrict__ block_tables, int num_seqs, int max_blocks,
@@ -182,41 +234,37 @@ write_tokens_fp8_kernel(const int32_t* __restrict__ block_tables, int num_seqs, 
   __shared__ int64_t s_slot[kTokensPerWg];
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kTokensPerWg;
-  const bool staged = num_seqs + 1 <= kQslLds;
-  if (staged)
-    for (int i = tid; i <= num_seqs; i += 256) qs[i] = qsl[i];
-  __syncthreads();
-  if (tid < kTokensPerWg) {
-    const int t = t0 + tid;
-    int64_t slot = -1;
-    if (t < num_tokens) {
-      const int32_t* q = staged ? qs : qsl;
-      int lo = 0, hi = num_seqs;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (q[mid] <= t) lo = mid; else hi = mid;
-      }
-      const int p = positions[t];
-      if (num_seqs > 0 && t < q[lo + 1] && p >= 0) {
-        const int lb = p / block_size;
-        if (lb < max_blocks) {
-          const int phys = block_tables[(int64_t)lo * max_blocks + lb];
-          if (phys >= 0) slot = (int64_t)phys * block_size + (p - lb * block_size);
-        }
-      }
-      if (slots_out) slots_out[t] = slot;
-    }
-    s_slot[tid] = slot;
-  }
-  __syncthreads();
-  const int n = min(kTokensPerWg, num_tokens - t0) * row_vecs;
-  for (int i = tid; i < n; i += 256) {
+  const int n = min(kTokensPerWg, num_tokens - t0) * row_vecs;   // output vectors of this workgroup
+  const int64_t base = (int64_t)t0 * row_vecs;
+  QuantIn<BF16IN> ka[kQuantAhead], va[kQuantAhead];
+  workgroup_slots(block_tables, num_seqs, max_blocks, positions, qsl, num_tokens, block_size, slots_out, t0, qs,
+                  s_slot, [&] {
+#pragma unroll
+                    for (int u = 0; u < kQuantAhead; ++u) {
+                      const int i = tid + 256 * u;
+                      if (i < n) {
+                        ka[u].load(key, base + i);
+                        va[u].load(value, base + i);
+                      }
+                    }
+                  });
+  auto store = [&](int i, const QuantIn<BF16IN>& k, const QuantIn<BF16IN>& v) {
     const int tl = i / row_vecs, cvec = i - tl * row_vecs;
     const int64_t slot = s_slot[tl];
-    if (slot < 0 || slot >= num_slots) continue;
-    const int64_t src = (int64_t)(t0 + tl) * row_vecs + cvec;
-    key_cache[slot * row_vecs + cvec] = quant16<BF16IN>(key, src, k_inv);
-    value_cache[slot * row_vecs + cvec] = quant16<BF16IN>(value, src, v_inv);
+    if (slot < 0 || slot >= num_slots) return;
+    key_cache[slot * row_vecs + cvec] = k.quant(k_inv);
+    value_cache[slot * row_vecs + cvec] = v.quant(v_inv);
+  };
+#pragma unroll
+  for (int u = 0; u < kQuantAhead; ++u) {
+    const int i = tid + 256 * u;
+    if (i < n) store(i, ka[u], va[u]);
+  }
+  for (int i = tid + 256 * kQuantAhead; i < n; i += 256) {
+    QuantIn<BF16IN> k, v;
+    k.load(key, base + i);
+    v.load(value, base + i);
+    store(i, k, v);
   }
 }
 
