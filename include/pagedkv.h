@@ -339,9 +339,13 @@ int pkv_swap_blocks(const void* src_key, const void* src_value, void* dst_key, v
  * it off.
  *
  * pkv_set_decode_workers: number of workers (wavefronts) the decode split
- * uses; 0 restores the default (compute units x pkv_get_waves_per_cu()).
- * The workspace size follows the setting.  Used by tests to force many
- * different split points.  Returns the previous value.
+ * uses; 0 restores the default (compute units x pkv_get_waves_per_cu(),
+ * lowered for a call whose block tables hold fewer chunks than that: at most
+ * num_seqs x KV heads x ceil(group / 16) x ceil(max_blocks_per_seq x
+ * block_size / 32) plus the segment cost per pair).  A forced count is used
+ * as given.  The workspace size follows the setting (sized for the full
+ * default count).  Used by tests to force many different split points.
+ * Returns the previous value.
  *
  * pkv_set_waves_per_cu: default worker density per compute unit (4..16,
  * multiple of 4; default 4).  Returns the previous value.
