@@ -47,6 +47,13 @@
  *   Support.  head_dim in {64, 128}; block_size in {16, 32};
  *             num_q_heads % num_kv_heads == 0.  Other values return
  *             PKV_EUNSUPPORTED.
+ *   Limits.   A token row (num_kv_heads * head_dim elements; for the E4M3
+ *             writes, of the float32 or bfloat16 input) of at most 2^31 - 1
+ *             bytes, block tables of at most 2^31 - 1 tokens
+ *             (max_blocks_per_seq * block_size), and pools (and block-copy
+ *             pools) under 2^62 bytes: the kernels' index arithmetic is exact
+ *             inside these bounds, and larger arguments return
+ *             PKV_EUNSUPPORTED before anything is enqueued.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H

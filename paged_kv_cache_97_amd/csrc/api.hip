@@ -2,6 +2,7 @@
 // Every check runs on the host before anything is enqueued.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdint.h>
 #include <string.h>
 
 #include <atomic>
@@ -38,6 +39,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int elem_bytes(pkv_dtype dt) { return dt == PKV_BF16 ? 2 : 4; }
 
+// Limits that keep the kernels' index arithmetic exact: a token row (all KV
+// heads of one token) of at most 2^31 - 1 bytes, since the kernels count row
+// vectors in 32 bits, and a pool of blocks x block_bytes well inside int64
+// (2^62 bytes), since they form byte and element offsets as block id x block
+// size in 64 bits.
+bool row_fits(int64_t row_bytes) { return row_bytes <= INT32_MAX; }
+bool pool_addressable(int64_t blocks, int64_t block_bytes) {
+  return (__int128)blocks * block_bytes < ((__int128)1 << 62);
+}
+
 int hip_fail(hipError_t e, const char* what) {
   return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -62,6 +73,21 @@ int decode_workers(int64_t max_chunks = INT64_MAX) {
   if (cus <= 0) cus = 256;
   const int64_t full = (int64_t)cus * g_waves_per_cu.load();
   return (int)std::max<int64_t>(1, std::min(full, max_chunks));
+}
+
+// Attention calls: the table width in tokens (max_blocks_per_seq x
+// block_size) is a 32-bit count in the kernels, like seq_lens, and the pools
+// must be addressable.  Call after check_shape.
+int check_attention_bounds(int32_t max_blocks_per_seq, int32_t block_size, int64_t num_blocks,
+                           int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype) {
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "block tables of %d blocks of %d tokens exceed 2^31 - 1 tokens", max_blocks_per_seq,
+                block_size);
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * (dtype == PKV_FP8_E4M3 ? 1 : elem_bytes(dtype));
+  if (!row_fits(row_bytes) || !pool_addressable(num_blocks, (int64_t)block_size * row_bytes))
+    return fail(PKV_EUNSUPPORTED, "pool too large to address (%lld blocks of %d rows of %lld bytes)",
+                (long long)num_blocks, block_size, (long long)row_bytes);
+  return PKV_OK;
 }
 
 int check_shape(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -186,6 +212,9 @@ int pkv_reshape_and_cache(const void* key, const void* value, void* key_cache, v
   if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "dtype %d", (int)dtype);
   const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * elem_bytes(dtype);
   if (row_bytes % 16) return fail(PKV_EUNSUPPORTED, "token row of %lld bytes is not a multiple of 16", (long long)row_bytes);
+  if (!row_fits(row_bytes) || !pool_addressable(num_blocks, (int64_t)block_size * row_bytes))
+    return fail(PKV_EUNSUPPORTED, "pool too large to address (%lld blocks of %d rows of %lld bytes)",
+                (long long)num_blocks, block_size, (long long)row_bytes);
   if (num_tokens == 0) return ok();
   if (!key || !value || !key_cache || !value_cache || !slot_mapping) return fail(PKV_EINVAL, "null pointer");
   if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
@@ -209,6 +238,9 @@ int pkv_write_new_tokens(const int32_t* block_tables, int32_t num_seqs, int32_t 
   if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "dtype %d", (int)dtype);
   const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * elem_bytes(dtype);
   if (row_bytes % 16) return fail(PKV_EUNSUPPORTED, "token row of %lld bytes is not a multiple of 16", (long long)row_bytes);
+  if (!row_fits(row_bytes) || !pool_addressable(num_blocks, (int64_t)block_size * row_bytes))
+    return fail(PKV_EUNSUPPORTED, "pool too large to address (%lld blocks of %d rows of %lld bytes)",
+                (long long)num_blocks, block_size, (long long)row_bytes);
   if (num_tokens == 0) return ok();
   if (!positions || !query_start_loc || !key || !value || !key_cache || !value_cache ||
       (num_seqs > 0 && max_blocks_per_seq > 0 && !block_tables))
@@ -228,9 +260,13 @@ static int check_fp8_write(int32_t num_tokens, int32_t num_kv_heads, int32_t hea
                 num_tokens, num_kv_heads, head_dim, (long long)num_blocks, block_size);
   if (in_dtype != PKV_F32 && in_dtype != PKV_BF16)
     return fail(PKV_EUNSUPPORTED, "key/value dtype %d (bf16 or f32)", (int)in_dtype);
-  if (((int64_t)num_kv_heads * head_dim) % 16)
-    return fail(PKV_EUNSUPPORTED, "token row of %lld elements is not a multiple of 16",
-                (long long)num_kv_heads * head_dim);
+  const int64_t row_elems = (int64_t)num_kv_heads * head_dim;   // E4M3 rows: one byte per element
+  if (row_elems % 16)
+    return fail(PKV_EUNSUPPORTED, "token row of %lld elements is not a multiple of 16", (long long)row_elems);
+  // the unquantised input rows (up to 4 bytes per element) must fit too
+  if (!row_fits(4 * row_elems) || !pool_addressable(num_blocks, (int64_t)block_size * row_elems))
+    return fail(PKV_EUNSUPPORTED, "pool too large to address (%lld blocks of %d rows of %lld elements)",
+                (long long)num_blocks, block_size, (long long)row_elems);
   if (!good_scale(k_scale) || !good_scale(v_scale))
     return fail(PKV_EINVAL, "k_scale %g / v_scale %g must be positive and finite", k_scale, v_scale);
   return PKV_OK;
@@ -282,6 +318,9 @@ int pkv_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_map
     return fail(PKV_EINVAL, "bad size (pairs %d, blocks %lld, block_bytes %lld)", num_pairs,
                 (long long)num_blocks, (long long)block_bytes);
   if (block_bytes % 16) return fail(PKV_EINVAL, "block_bytes %lld is not a multiple of 16", (long long)block_bytes);
+  if (!pool_addressable(num_blocks, block_bytes))
+    return fail(PKV_EUNSUPPORTED, "pool too large to address (%lld blocks of %lld bytes)", (long long)num_blocks,
+                (long long)block_bytes);
   if (num_pairs == 0) return ok();
   if (!key_cache || !value_cache || !block_mapping) return fail(PKV_EINVAL, "null pointer");
   if (!aligned16(key_cache) || !aligned16(value_cache)) return fail(PKV_EINVAL, "pools must be 16-byte aligned");
@@ -323,6 +362,9 @@ int pkv_swap_blocks(const void* src_key, const void* src_value, void* dst_key, v
     return fail(PKV_EINVAL, "bad size (pairs %d, blocks %lld/%lld, block_bytes %lld)", num_pairs,
                 (long long)src_num_blocks, (long long)dst_num_blocks, (long long)block_bytes);
   if (block_bytes % 16) return fail(PKV_EINVAL, "block_bytes %lld is not a multiple of 16", (long long)block_bytes);
+  if (!pool_addressable(src_num_blocks, block_bytes) || !pool_addressable(dst_num_blocks, block_bytes))
+    return fail(PKV_EUNSUPPORTED, "pool too large to address (%lld / %lld blocks of %lld bytes)",
+                (long long)src_num_blocks, (long long)dst_num_blocks, (long long)block_bytes);
   if (num_pairs == 0) return ok();
   if (!src_key || !dst_key || !block_mapping) return fail(PKV_EINVAL, "null pointer");
   if ((src_value == nullptr) != (dst_value == nullptr))
@@ -408,6 +450,8 @@ static int decode_impl(float* out, const void* query, const void* key_cache, con
   if (num_seqs < 0 || num_seqs > kMaxSeqs) return fail(PKV_EUNSUPPORTED, "num_seqs %d (max %d)", num_seqs, kMaxSeqs);
   if (max_blocks_per_seq < 0 || num_blocks < 0 || max_seq_len < 0)
     return fail(PKV_EINVAL, "negative size");
+  st = check_attention_bounds(max_blocks_per_seq, block_size, num_blocks, num_kv_heads, head_dim, dtype);
+  if (st != PKV_OK) return st;
   if (num_seqs == 0) return ok();
   if (!out || !query || !seq_lens || (max_blocks_per_seq > 0 && (!block_tables || !key_cache || !value_cache)))
     return fail(PKV_EINVAL, "null pointer");
@@ -503,6 +547,8 @@ static int varlen_impl(float* out, const void* query, const void* key_cache, con
   if (num_tokens < 0 || max_query_len < 0 || max_blocks_per_seq < 0 || num_blocks < 0 || max_seq_len < 0)
     return fail(PKV_EINVAL, "negative size");
   if (num_tokens > 0 && max_query_len == 0) return fail(PKV_EINVAL, "max_query_len is 0 with %d tokens", num_tokens);
+  st = check_attention_bounds(max_blocks_per_seq, block_size, num_blocks, num_kv_heads, head_dim, dtype);
+  if (st != PKV_OK) return st;
   if (num_seqs == 0 || num_tokens == 0) return ok();
   if (!out || !query || !seq_lens || !query_start_loc ||
       (max_blocks_per_seq > 0 && (!block_tables || !key_cache || !value_cache)))

@@ -171,3 +171,38 @@ def test_stream_read_validation():
     assert lib.pkv_stream_read(ctypes.c_void_p((1 << 20) + 8), 32, ctypes.c_void_p(1 << 20), 4, None) == 1
     for bad in (0, 6, 262148):
         assert lib.pkv_stream_read(ctypes.c_void_p(1 << 20), 32, ctypes.c_void_p(1 << 20), bad, None) == 1
+
+
+def test_sizes_beyond_the_kernels_index_range_are_refused():
+    """Arguments whose products would overflow the kernels' index arithmetic
+    (token rows past 2^31 - 1 bytes, tables past 2^31 - 1 tokens, pools of
+    2^62 bytes or more) are refused with EUNSUPPORTED before any launch."""
+    lib = ops.lib()
+    huge = 1 << 50
+    # decode: the table width in tokens, then the pool size
+    assert _decode(lib, max_blocks=1 << 27) == 2
+    assert _decode(lib, NB=huge) == 2 and b"pool" in lib.pkv_last_error()
+    assert _step(lib, True, NB=huge) == 2
+    # varlen: the same two limits
+    p = ctypes.c_void_p(1 << 20)
+
+    def varlen(max_blocks, nb):
+        return lib.pkv_paged_attention_varlen(p, p, p, p, p, max_blocks, p, p, 2, 3, 2, 64, 8, 2, 128, nb, 16, 0.1, 1,
+                                              p, 1 << 30, None)
+    assert varlen(1 << 27, 16) == 2
+    assert varlen(4, huge) == 2
+    # cache writes: pool size and row size
+    assert lib.pkv_reshape_and_cache(None, None, None, None, None, 3, 8, 128, huge, 16, 1, None) == 2
+    assert lib.pkv_reshape_and_cache(None, None, None, None, None, 3, 1 << 20, 1 << 11, 16, 16, 0, None) == 2
+    args = [None, 2, 4, None, None, 3, 16, None, None, None, None, 8, 128, huge, 1, None, None]
+    assert lib.pkv_write_new_tokens(*args) == 2
+    nul = [None] * 5
+    assert lib.pkv_reshape_and_cache_fp8(*nul, 3, 1 << 20, 1 << 10, 16, 16, 0, 0.5, 0.5, None) == 2
+    assert lib.pkv_reshape_and_cache_fp8(*nul, 3, 8, 128, huge, 16, 1, 0.5, 0.5, None) == 2
+    # whole-block copies
+    assert lib.pkv_copy_blocks(None, None, None, 2, huge, 1 << 20, None) == 2
+    assert lib.pkv_swap_blocks(None, None, None, None, None, 3, 4, huge, 1 << 20, None) == 2
+    # the largest legal sizes of the same calls still pass these checks (and
+    # stop at the null pointers instead)
+    assert lib.pkv_reshape_and_cache(None, None, None, None, None, 3, 8, 128, 1 << 30, 16, 1, None) == 1
+    assert lib.pkv_copy_blocks(None, None, None, 2, 1 << 30, 1 << 20, None) == 1
