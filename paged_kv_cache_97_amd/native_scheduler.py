@@ -38,9 +38,13 @@ class _Plan(ctypes.Structure):
 
 
 def _arr(ptr, n: int, dtype) -> np.ndarray:
-    if n <= 0:
-        return np.zeros(0, dtype)
-    return np.ctypeslib.as_array(ptr, shape=(n,)).copy()
+    """A copy of n elements at ptr.  One memmove into a fresh array:
+    numpy.ctypeslib.as_array would build a new ctypes array and pointer type
+    for every call (≈ 0.15 ms each, most of a step's host time)."""
+    out = np.empty(max(n, 0), dtype)
+    if n > 0:
+        ctypes.memmove(out.ctypes.data, ctypes.cast(ptr, ctypes.c_void_p).value, out.nbytes)
+    return out
 
 
 class NativeStepPlan:
