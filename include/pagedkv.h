@@ -22,9 +22,9 @@
  *             knobs.  Buffers must stay alive until the enqueued work ends.
  *   Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
  *             stream).  Calls only enqueue kernels, in stream order, and never
- *             synchronise: one or two per call, four for a varlen call that
- *             has both prefill-chunk and decode rows (prefill plan, prefill,
- *             decode split, merge).
+ *             synchronise: one or two per call, three for a varlen call
+ *             with prefill-chunk rows (decode split, merge -- which also
+ *             builds the prefill kernel's item plan -- then prefill).
  *   Errors.   Arguments are validated on the host before anything is
  *             enqueued: a call that returns non-zero has enqueued nothing,
  *             except PKV_EHIP (the launch itself failed).  pkv_last_error()

@@ -396,7 +396,8 @@ static int run_decode(float* out, const void* query, const void* key_cache, cons
                       const int32_t* qsl, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t max_seq_len,
                       float scale, KvFormat fmt, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream, const void* new_k = nullptr, const void* new_v = nullptr) {
+                      hipStream_t stream, const void* new_k = nullptr, const void* new_v = nullptr,
+                      int* prefill_plan = nullptr) {
   const int group = num_q_heads / num_kv_heads;
   const int head_tiles = (group + 15) / 16;
   const int seg_chunks = g_seg_chunks.load();
@@ -433,6 +434,8 @@ static int run_decode(float* out, const void* query, const void* key_cache, cons
   a.new_v = new_v;
   a.k_inv = fmt.kind == pkv::KvKind::FP8 ? 1.0f / fmt.k_scale : 1.0f;
   a.v_inv = fmt.kind == pkv::KvKind::FP8 ? 1.0f / fmt.v_scale : 1.0f;
+  a.prefill_plan = prefill_plan;
+  a.prefill_max_tok = max_blocks_per_seq * block_size;
   pkv::decode_workspace_carve(a, workspace, head_dim);
   (void)max_seq_len;
   hipError_t e = pkv::launch_decode(a, head_dim, block_size, fmt.kind, stream, g_ev_start, g_ev_stop);
@@ -568,6 +571,21 @@ static int varlen_impl(float* out, const void* query, const void* key_cache, con
       return fail(PKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
   }
+  int* plan = reinterpret_cast<int*>(static_cast<char*>(workspace) + dec_bytes);
+  const bool lds_prefill = max_query_len > 1 && pkv::prefill_uses_plan(head_dim, fmt.kind);
+  // Decode rows (sequences with exactly one query row) first, through the
+  // split and merge kernels; the merge launch also builds the prefill
+  // kernel's item plan (one extra workgroup), so no launch of its own.
+  hipEvent_t e0 = g_ev_start, e1 = g_ev_stop;
+  g_ev_start = nullptr;
+  g_ev_stop = nullptr;
+  int rc = run_decode(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens,
+                      query_start_loc, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                      max_seq_len, scale, fmt, workspace, workspace_bytes, s, nullptr, nullptr,
+                      lds_prefill ? plan : nullptr);
+  g_ev_start = e0;
+  g_ev_stop = e1;
+  if (rc != PKV_OK) return rc;
   // profile events (if set) bracket the prefill kernel, the step's dominant one
   if (g_ev_start) (void)hipEventRecord(g_ev_start, s);
   if (max_query_len > 1) {
@@ -589,21 +607,12 @@ static int varlen_impl(float* out, const void* query, const void* key_cache, con
     p.v_scale = fmt.v_scale;
     const int cus = current_cus();
     p.waves = (cus > 0 ? cus : 256) * 4;
-    p.plan = reinterpret_cast<int*>(static_cast<char*>(workspace) + dec_bytes);
+    p.plan = plan;
     hipError_t e = pkv::launch_prefill(p, head_dim, block_size, fmt.kind, cus, s);
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
   }
   if (g_ev_stop) (void)hipEventRecord(g_ev_stop, s);
-  // decode rows (sequences with exactly one query row) through the split kernels
-  hipEvent_t e0 = g_ev_start, e1 = g_ev_stop;
-  g_ev_start = nullptr;
-  g_ev_stop = nullptr;
-  int rc = run_decode(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens,
-                      query_start_loc, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
-                      max_seq_len, scale, fmt, workspace, workspace_bytes, s);
-  g_ev_start = e0;
-  g_ev_stop = e1;
-  return rc;
+  return ok();
 }
 
 int pkv_paged_attention_varlen(float* out, const void* query, const void* key_cache,

@@ -49,6 +49,7 @@
 #include "common.h"
 #include "launch.h"
 #include "tiles.h"
+#include "prefill_plan.h"
 
 namespace pkv {
 
@@ -316,6 +317,10 @@ template <int D>
 __global__ void __launch_bounds__(256) decode_reduce_kernel(const DecodeArgs a) {
   const int ppseq = a.num_kv_heads * a.head_tiles;
   const int pair = blockIdx.x;
+  if (pair == a.num_seqs * ppseq) {                    // the extra workgroup: the prefill rows' item plan
+    build_prefill_plan(a.qsl, a.seq_lens, a.num_seqs, a.prefill_max_tok, a.num_kv_heads, a.group, a.prefill_plan);
+    return;
+  }
   const int s = pair / ppseq, pr = pair - s * ppseq;
   if (a.qsl != nullptr && a.qsl[s + 1] - a.qsl[s] != 1) return;
   const int h = pr / a.head_tiles, ht = pr - h * a.head_tiles;
@@ -398,7 +403,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream, hipEv
   if (err != hipSuccess) return err;
   const int pairs = a.num_seqs * a.num_kv_heads * a.head_tiles;
   if (pairs > 0)
-    hipLaunchKernelGGL(decode_reduce_kernel<Tile::D>, dim3(pairs), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(decode_reduce_kernel<Tile::D>, dim3(pairs + (a.prefill_plan != nullptr ? 1 : 0)), dim3(256), 0,
+                       stream, a);
   return hipGetLastError();
 }
 

@@ -48,6 +48,11 @@ struct DecodeArgs {
   const void* new_v;
   float k_inv;
   float v_inv;
+  // Optional (varlen calls whose prefill rows use the workgroup-shared
+  // kernel): the merge launch carries one more workgroup that builds that
+  // kernel's item plan here, for tables of prefill_max_tok tokens.
+  int* prefill_plan;
+  int prefill_max_tok;
   // workspace
   int* cum;                   // [B + 1] chunk prefix sums (written by the split kernel)
   float* part_ml;             // [slots, tile_cols, 2]  (max, sum) in the log2 domain
@@ -111,10 +116,13 @@ struct PrefillArgs {
 size_t prefill_plan_bytes(int num_seqs);
 
 // Dispatches to the workgroup-shared kernel (bf16 or FP8 pools, head_dim 128;
-// plan kernel first) or the per-wave kernel (other shapes).
+// its plan built beforehand) or the per-wave kernel (other shapes).
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, KvKind kind, int cus,
                           hipStream_t stream);
 hipError_t launch_prefill_lds(const PrefillArgs& a, int block_size, bool fp8, int cus, hipStream_t stream);
+// Whether launch_prefill takes the workgroup-shared kernel, whose item plan
+// (PrefillArgs::plan) must have been built beforehand (DecodeArgs::prefill_plan).
+bool prefill_uses_plan(int head_dim, KvKind kind);
 
 // Whole-block copies for every (src, dst) pair of mapping (int64 [pairs][2]);
 // src1/dst1 may be null (one pool).  Pairs with an id outside its pool are

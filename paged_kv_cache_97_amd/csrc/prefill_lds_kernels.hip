@@ -19,13 +19,15 @@
 //    than 2^8 (the rescale is exact; weights up to 256 are fine in bf16/fp32),
 //    and that rare rescale runs outside the hot chunk loop;
 //  * items are taken from a work counter in order of decreasing sequence
-//    length (the plan kernel sorts up to 512 prefill sequences), so the
+//    length (the plan, built by one extra workgroup of the decode merge launch
+//    just before, sorts up to 512 prefill sequences), so the
 //    longest items start first.
 #include <type_traits>
 
 #include "common.h"
 #include "launch.h"
 #include "tiles.h"
+#include "prefill_plan.h"
 
 namespace pkv {
 
@@ -35,8 +37,7 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfTiles = 2;                        // 16-column tiles per wave
 constexpr int kPfWaveCols = 16 * kPfTiles;         // 64
 constexpr int kPfCols = kPfWaveCols * kPfWaves;    // 256 columns per item
-constexpr int kPlanHeader = 16;                    // ints: [0] items, [1] prefill seqs, [2] counter
-constexpr int kSortMax = 512;
+static_assert(kPfCols == kPlanItemCols, "the plan counts items of the kernel's width");
 constexpr float kRescaleSlack = 8.f;               // log2 units
 }  // namespace
 
@@ -44,78 +45,6 @@ constexpr float kRescaleSlack = 8.f;               // log2 units
 // [B], their item prefix sums [B + 1], and scan scratch [B + 1].
 size_t prefill_plan_bytes(int num_seqs) {
   return ((size_t)(kPlanHeader + 3 * (size_t)num_seqs + 2) * 4 + 255) / 256 * 256;
-}
-
-// Exclusive scan of f(i), i in [0, n), writing out(i, prefix) for i in [0, n]
-// (out(n, total)); LDS use is independent of n.  Ends with a barrier.
-template <typename F, typename O>
-__device__ int block_scan_to(int n, F f, O out) {
-  __shared__ int wave_tot[256 / kWave];
-  const int tid = threadIdx.x, wid = tid / kWave;
-  int carry = 0;
-  for (int base = 0; base < n; base += 256) {
-    const int i = base + tid;
-    const int v = i < n ? f(i) : 0;
-    int x = wave_inclusive_scan(v);
-    if (lane_id() == kWave - 1) wave_tot[wid] = x;
-    __syncthreads();
-    int off = carry;
-    for (int w = 0; w < wid; ++w) off += wave_tot[w];
-    if (i < n) out(i, x + off - v);
-    int tot = 0;
-    for (int w = 0; w < 256 / kWave; ++w) tot += wave_tot[w];
-    carry += tot;
-    __syncthreads();
-  }
-  if (tid == 0) out(n, carry);
-  __syncthreads();
-  return carry;
-}
-
-__global__ void __launch_bounds__(256)
-prefill_plan_kernel(const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int B, int max_tok,
-                    int Hkv, int G, int* __restrict__ plan) {
-  __shared__ int s_len[kSortMax];
-  __shared__ int s_seq[kSortMax];
-  int* order = plan + kPlanHeader;
-  int* cum = order + B;
-  int* pre = cum + B + 1;                              // scratch: prefix of "is prefill"
-  auto is_prefill = [&](int s) { return qsl[s + 1] - qsl[s] > 1 ? 1 : 0; };
-  const int P = block_scan_to(B, is_prefill, [&](int i, int v) { pre[i] = v; });
-  auto len = [&](int s) {
-    const int L = seq_lens[s];
-    return L < 0 ? 0 : (L > max_tok ? max_tok : L);
-  };
-  if (P <= kSortMax) {
-    for (int s = threadIdx.x; s < B; s += 256)
-      if (pre[s + 1] != pre[s]) {
-        s_seq[pre[s]] = s;
-        s_len[pre[s]] = len(s);
-      }
-    __syncthreads();
-    // rank: longer first, ties by sequence index
-    for (int i = threadIdx.x; i < P; i += 256) {
-      int rank = 0;
-      for (int j = 0; j < P; ++j)
-        rank += (s_len[j] > s_len[i]) || (s_len[j] == s_len[i] && j < i);
-      order[rank] = s_seq[i];
-    }
-  } else {
-    for (int s = threadIdx.x; s < B; s += 256)
-      if (pre[s + 1] != pre[s]) order[pre[s]] = s;
-  }
-  __syncthreads();
-  auto items = [&](int r) {
-    const int s = order[r];
-    const int q = qsl[s + 1] - qsl[s];
-    return Hkv * ((q * G + kPfCols - 1) / kPfCols);
-  };
-  const int total = block_scan_to(P, items, [&](int i, int v) { cum[i] = v; });
-  if (threadIdx.x == 0) {
-    plan[0] = total;
-    plan[1] = P;
-    plan[2] = 0;                                       // work counter
-  }
 }
 
 // max(a, b) as one v_max_f32.  The compiler's fmaxf quiets signalling NaNs
@@ -497,10 +426,6 @@ prefill_lds_kernel(const PrefillArgs a) {
 }
 
 hipError_t launch_prefill_lds(const PrefillArgs& a, int block_size, bool fp8, int cus, hipStream_t stream) {
-  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(256), 0, stream, a.qsl, a.seq_lens, a.num_seqs,
-                     a.max_blocks * block_size, a.num_kv_heads, a.group, a.plan);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int grid = cus > 0 ? cus : 256;
   if (block_size == 16 && !fp8)
     hipLaunchKernelGGL((prefill_lds_kernel<16, false>), dim3(grid), dim3(kPfThreads), 0, stream, a);

@@ -231,9 +231,13 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+bool prefill_uses_plan(int head_dim, KvKind kind) {
+  return (kind == KvKind::BF16 || kind == KvKind::FP8) && head_dim == 128;
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, KvKind kind, int cus,
                           hipStream_t stream) {
-  if ((kind == KvKind::BF16 || kind == KvKind::FP8) && head_dim == 128)
+  if (prefill_uses_plan(head_dim, kind))
     return launch_prefill_lds(a, block_size, kind == KvKind::FP8, cus, stream);
 #define PKV_CASE(T, B, D, BS) \
   if (head_dim == D && block_size == BS) return launch_prefill_t<T<D, BS>, PrefillTiles<B, D>::value>(a, stream);

@@ -77,7 +77,7 @@ def test_any_finite_scale(name, scale, dev):
 
 
 def test_more_prefill_sequences_than_the_plan_sorts(dev):
-    """600 prefill chunks in one step: past the 512 the plan kernel orders by
+    """600 prefill chunks in one step: past the 512 the plan orders by
     length, the work items follow the batch order instead."""
     spec = _mixed(num_decode=20, num_prefill=600, prefill_chunk=3, prefill_ctx=("uniform", 0, 40))
     _check(W.generate(spec, seed=43), dev, "600 prefills")
