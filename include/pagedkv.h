@@ -185,8 +185,11 @@ size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   block_tables int32 [num_seqs, max_blocks_per_seq]; seq_lens int32 [num_seqs]
  *   seq_lens[s] == 0 gives a zero row.  seq_lens are clamped to
  *   max_blocks_per_seq*block_size; block ids to [0, num_blocks).
- *   max_seq_len  an upper bound of seq_lens (host scalar, used for sizing;
- *                0 is allowed and then every row is zero).
+ *   max_seq_len  the caller's upper bound of seq_lens (host scalar).  It
+ *                must be >= 0 and is otherwise not used: it neither sizes the
+ *                workspace nor clamps seq_lens (seq_lens are only clamped to
+ *                max_blocks_per_seq*block_size, as above), so a value below
+ *                the true lengths changes nothing.
  *   workspace    >= pkv_decode_workspace_size(...) bytes, 256-byte aligned,
  *                contents ignored on entry.  Long sequences are split over
  *                several workers (split-K); a second kernel merges the parts.

@@ -612,3 +612,62 @@ def test_fp8_write_then_decode_equals_dense_attention_of_dequantised_tokens():
         v = oracle.e4m3_value(oracle.quantize_kv(wl.logical_v[s][:L], "bf16", vs)) * vs
         ref = _sdpa_reference(oracle.to_f64(wl.query[s:s + 1], "bf16"), k, v, wl.scale, [L], G)[0]
         np.testing.assert_allclose(got[s], ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- bf16 widening
+def _widen_bf16_by_shift_of(x, shift):
+    bits = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(shift)
+    return bits.view(np.float32).astype(np.float64)
+
+
+def _torch_bf16_to_f64(bits):
+    return torch.from_numpy(np.asarray(bits, dtype=np.uint16).view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+
+
+def _bf16_decodings_agree(ref, got):
+    nan_ref, nan_got = np.isnan(ref), np.isnan(got)
+    return bool(np.array_equal(nan_ref, nan_got)
+                and np.array_equal(ref[~nan_ref].view(np.uint64), got[~nan_got].view(np.uint64)))
+
+
+@pytest.mark.filterwarnings("ignore:invalid value encountered in cast")
+def test_bf16_widening_equals_torch_bfloat16_on_every_bit_pattern():
+    """to_f64(bits, 'bf16') is how the oracle reads every bf16 query, key and
+    value.  torch's own bfloat16 -> float64 conversion decodes all 65,536 bit
+    patterns: the oracle must agree bit for bit on every non-NaN pattern and on
+    which patterns are NaN.  A planted widening that shifts by 8 instead of 16
+    fails the same comparison."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = _torch_bf16_to_f64(bits)
+    assert np.isnan(ref).sum() == 2 * 127              # exponent all ones, nonzero mantissa, both signs
+    assert _bf16_decodings_agree(ref, oracle.to_f64(bits, "bf16"))
+    # fixed points of the format: 1.0 = 0x3F80, -2.0 = 0xC000, +inf = 0x7F80,
+    # the smallest subnormal 2^-133 = 0x0001, -0.0 = 0x8000
+    fixed = {0x3F80: 1.0, 0xC000: -2.0, 0x7F80: math.inf, 0x0001: 2.0 ** -133, 0x0000: 0.0}
+    for b, v in fixed.items():
+        assert oracle.to_f64(np.array([b], np.uint16), "bf16")[0] == v
+    assert math.copysign(1.0, oracle.to_f64(np.array([0x8000], np.uint16), "bf16")[0]) == -1.0
+    assert not _bf16_decodings_agree(ref, _widen_bf16_by_shift_of(bits, 8))
+
+
+def test_generator_bf16_rounding_equals_torch_cast():
+    """The seeded generators round float32 normals to bf16 by round-to-nearest-
+    even; torch's float32 -> bfloat16 cast is that rounding.  Checked on random
+    values, on every exact tie between bf16 neighbours near 1 (both ways, both
+    signs) and on the floats just beside each tie."""
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(200_000).astype(np.float32),
+                        (rng.standard_normal(20_000) * 1e30).astype(np.float32),
+                        (rng.standard_normal(20_000) * 1e-35).astype(np.float32)])
+    # ties: float32 patterns whose low 16 bits are exactly 0x8000, plus neighbours
+    hi = (np.arange(0x3F00, 0x4100, dtype=np.uint32) << 16)
+    tie = hi | np.uint32(0x8000)
+    ties = np.concatenate([tie, tie - 1, tie + 1, tie | np.uint32(0x80000000)]).view(np.float32)
+    x = np.concatenate([x, ties])
+    got = W._to_bf16_bits(x)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+    # ties to even: 1 + 2^-8 (halfway between 1.0 and 1 + 2^-7) goes down to 1.0,
+    # 1 + 3 * 2^-8 goes up to 1 + 2^-6
+    assert W._to_bf16_bits(np.array([1 + 2.0 ** -8], np.float32))[0] == 0x3F80
+    assert W._to_bf16_bits(np.array([1 + 3 * 2.0 ** -8], np.float32))[0] == 0x3F82
