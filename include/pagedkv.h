@@ -257,6 +257,31 @@ int pkv_decode_step_fp8(float* out, const void* query, const void* key, const vo
                         float k_scale, float v_scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Allocation-free decode attention, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same computation, arguments (less
+ * the workspace), layouts and errors as pkv_paged_attention_decode (F32 or
+ * BF16 pools), and the same kernels.  The split-K workspace lives in a
+ * static device array of the library of pkv_noalloc_scratch_bytes() bytes
+ * (16 MiB) that every device running this call holds until the process ends;
+ * the call itself allocates nothing.  A call that would need more scratch
+ * (pkv_decode_workspace_size(...) above that size, e.g. more than about 3,000
+ * sequences x KV heads of 8 heads per group) returns PKV_EUNSUPPORTED
+ * before anything is enqueued.  All calls on one device share that array:
+ * calls that overlap on one device (other streams, other host threads
+ * without ordering) race and give wrong results; calls in one stream are
+ * ordered and safe.  Nothing in it needs clearing between calls.
+ */
+int pkv_paged_attention_decode_noalloc(float* out, const void* query, const void* key_cache,
+                                       const void* value_cache, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
+                                       pkv_dtype dtype, void* stream);
+/* Size in bytes of the static scratch of pkv_paged_attention_decode_noalloc. */
+size_t pkv_noalloc_scratch_bytes(void);
+
+/*
  * Bytes of device workspace pkv_paged_attention_varlen needs (current device).
  */
 size_t pkv_varlen_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,

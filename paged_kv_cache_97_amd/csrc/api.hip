@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <cmath>
 
 #include "../../include/pagedkv.h"
@@ -520,6 +521,74 @@ int pkv_decode_step_fp8(float* out, const void* query, const void* key, const vo
                      num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_seq_len, scale,
                      PKV_FP8_E4M3, KvFormat{pkv::KvKind::FP8, k_scale, v_scale}, workspace, workspace_bytes,
                      stream, key, value);
+}
+
+// ---------------------------------------------------------------- allocation-free decode
+// Device scratch of pkv_paged_attention_decode_noalloc: the split-K workspace
+// (chunk prefix sums, part maxima and sums, partial outputs) of one call.
+// Each device that runs the entry point holds its own copy until the process
+// ends.  In host code `scratch` names a host-side stand-in, not device memory:
+// only the per-device address from hipGetSymbolAddress is ever passed on.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current.  Returns nullptr (and sets the error) on failure.
+void* device_scratch() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    hip_fail(e, "hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(PKV_EUNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+size_t pkv_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int pkv_paged_attention_decode_noalloc(float* out, const void* query, const void* key_cache,
+                                       const void* value_cache, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
+                                       pkv_dtype dtype, void* stream) {
+  if (dtype == PKV_FP8_E4M3)
+    return fail(PKV_EINVAL, "E4M3 pools need their scales: pkv_paged_attention_decode_noalloc takes F32 or BF16");
+  int st = check_shape(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_seqs > kMaxSeqs) return fail(PKV_EUNSUPPORTED, "num_seqs %d (max %d)", num_seqs, kMaxSeqs);
+  const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (need > kScratchBytes)
+    return fail(PKV_EUNSUPPORTED,
+                "pkv_paged_attention_decode_noalloc: this shape needs up to %zu bytes of scratch, the library's static "
+                "scratch holds %zu; use pkv_paged_attention_decode with a workspace",
+                need, kScratchBytes);
+  void* ws = device_scratch();
+  if (ws == nullptr) return PKV_EHIP;
+  return decode_impl(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_seq_len, scale, dtype,
+                     plain_format(dtype), ws, kScratchBytes, stream);
 }
 
 static size_t varlen_decode_part(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {

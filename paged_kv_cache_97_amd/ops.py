@@ -51,6 +51,10 @@ _SIGNATURES = {
     "pkv_decode_step_fp8": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32,
                                      _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_f32, _c_f32, _c_f32, _c_vp,
                                      _c_sz, _c_vp]),
+    "pkv_paged_attention_decode_noalloc": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32,
+                                                    _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_f32, _c_i32,
+                                                    _c_vp]),
+    "pkv_noalloc_scratch_bytes": (_c_sz, []),
     "pkv_sched_create": (_c_vp, [_c_vp, _c_vp]),
     "pkv_sched_destroy": (None, [_c_vp]),
     "pkv_sched_add_request": (_c_i32, [_c_vp, _c_i64, _c_i32, _c_i32]),
@@ -226,6 +230,32 @@ def paged_attention_decode(query: torch.Tensor, key_cache: torch.Tensor, value_c
         int(max_seq_len), float(scale), _kv_dtype(query), _dev(ws, "workspace"),
         ws.numel() * ws.element_size(), _stream(query)), "paged_attention_decode")
     return out
+
+
+def paged_attention_decode_noalloc(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                                   block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float, max_seq_len: int,
+                                   out: torch.Tensor) -> torch.Tensor:
+    """paged_attention_decode without a workspace: the library's allocation-free
+    entry point, whose split-K scratch is a static device array.  `out`
+    (float32 [B, Hq, D]) is required, so nothing is allocated on this path."""
+    B, Hq, D = query.shape
+    NB, bs, Hkv, Dk = key_cache.shape
+    if Dk != D or value_cache.shape != key_cache.shape:
+        raise ValueError("cache shapes disagree with the query")
+    if query.dtype != key_cache.dtype or value_cache.dtype != key_cache.dtype:
+        raise ValueError("query and caches must share one dtype")
+    if block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_tables/seq_lens must have num_seqs rows")
+    _check(lib().pkv_paged_attention_decode_noalloc(
+        _dev(out, "out", torch.float32, 3), _dev(query, "query", ndim=3), _dev(key_cache, "key_cache", ndim=4),
+        _dev(value_cache, "value_cache", ndim=4), _dev(block_tables, "block_tables", torch.int32, 2),
+        block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32, 1), B, Hq, Hkv, D, NB, bs,
+        int(max_seq_len), float(scale), _kv_dtype(query), _stream(query)), "paged_attention_decode_noalloc")
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().pkv_noalloc_scratch_bytes())
 
 
 def paged_attention_varlen(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,

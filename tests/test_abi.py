@@ -206,3 +206,21 @@ def test_sizes_beyond_the_kernels_index_range_are_refused():
     # stop at the null pointers instead)
     assert lib.pkv_reshape_and_cache(None, None, None, None, None, 3, 8, 128, 1 << 30, 16, 1, None) == 1
     assert lib.pkv_copy_blocks(None, None, None, 2, 1 << 30, 1 << 20, None) == 1
+
+
+def test_noalloc_decode_validation_runs_before_any_launch():
+    """The allocation-free decode call rejects E4M3 pools, unsupported shapes and
+    shapes whose split-K workspace exceeds its static scratch, on the host."""
+    lib = ops.lib()
+    assert lib.pkv_noalloc_scratch_bytes() == 16 << 20
+
+    def call(B=2, Hq=8, Hkv=2, D=128, bs=16, dtype=1):
+        p = 1 << 20
+        return lib.pkv_paged_attention_decode_noalloc(p, p, p, p, p, 4, p, B, Hq, Hkv, D, 16, bs, 64, 0.1, dtype,
+                                                      None)
+    assert call(dtype=2) == 1
+    assert call(D=96) == 2
+    assert call(Hq=7) == 1
+    assert call(B=9000) == 2
+    assert call(B=4096, Hq=64, Hkv=8) == 2
+    assert b"scratch" in lib.pkv_last_error()
