@@ -1,31 +1,36 @@
 """Benchmark of the paged KV-cache hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--no-cpu]
 
-A step is one decode iteration of the 128-sequence GQA workload (64 query /
-8 KV heads, head_dim 128, bf16 KV, 16-token blocks, lognormal lengths with
-median 1500 clipped to [16, 8192]): one pkv_decode_step call -- the split
-kernel, which also maps and writes the step's new tokens into their slots,
-then the merge kernel (--two-call: pkv_write_new_tokens, then
-pkv_paged_attention_decode).
-Inputs are resident in HBM before timing starts.  Prints one JSON line.
---config N runs another seeded workload the same way (1-4 decode; 5 is the
-mixed chunked-prefill + decode step, timed through the varlen call, whose
-dominant kernel is the MFMA-bound prefill kernel).  --blocks times the
-copy-on-write block copy and the swap to and from pinned host memory.
+Default: the headline line is workload 3, a decode iteration of the
+128-sequence GQA batch (64 query / 8 KV heads, head_dim 128, bf16 KV, 16-token
+blocks, lognormal lengths with median 1500 clipped to [16, 8192]): one
+pkv_decode_step call -- the split kernel, which also maps and writes the
+step's new tokens into their slots, then the merge kernel.  The same JSON
+line then carries, under "configs", every other workload timed the same way:
+1 (tiny fp32), 2 (MHA bf16), 3 with E4M3 pools, 4 (long contexts with a
+shared prefix; logical and unique bytes), 5 (the mixed chunked-prefill +
+decode step through write_new_tokens + the varlen call, whose dominant kernel
+is the MFMA-bound prefill kernel).  --config N times one workload alone.
+--blocks times the copy-on-write block copy and the swap to and from pinned
+host memory; --serve the step driver.  Inputs are resident in HBM before
+timing starts.
 
-value = KV bytes read per step / step time (GB/s, 1 GB = 1e9 B), where KV
-bytes = sum(seq_len) * 2 (K and V) * num_kv_heads * head_dim * 2 B -- each
-sequence's K/V read once per KV head, as GQA grouping allows.
-roofline.achieved = the same bytes / mean duration of the split kernel alone,
-from HIP events the library records around that kernel on its stream during a
-second pass of the same K steps (the events are kept out of the first, timed
-pass because each record adds a few microseconds of queue serialisation).
-cpu_baseline = the float64 oracle on a bounded sample of the same batch.
-cold_step_ms = the same step timed alone after 1 GiB of scratch was written
-(no cache holds the previous step's data); hbm_stream_read_GBps = the
-library's plain streaming read over 4 GiB (pkv_stream_read), the read rate
-this part reaches in practice.
+value = KV bytes read per step / mean step time over K back-to-back steps
+(GB/s, 1 GB = 1e9 B), where KV bytes = sum(seq_len) * 2 (K and V) *
+num_kv_heads * head_dim * element size -- each sequence's K/V read once per
+KV head, as GQA grouping allows.  step_ms = each step between its own events.
+roofline.achieved = the same bytes / mean duration of the dominant kernel
+alone, from HIP events the library records around it on its stream during a
+second pass of K steps.
+cpu_baseline = the float64 oracle over the whole step on a fork-started pool
+of worker processes (BLAS one thread each), before the GPU is touched; its
+first pass is also what every GPU row of the step is compared with
+(oracle_check).  Other workloads are checked on a sample of sequences.
+cold_step_ms = each step timed alone after a streaming read of 1 GiB of other
+data; cold_step_after_write_ms after an overwrite of 1 GiB; hbm_stream_read_GBps
+= the library's plain streaming read over 4 GiB (pkv_stream_read), the read
+rate this part reaches in practice.
 """
 from __future__ import annotations
 
@@ -141,50 +146,142 @@ def _fp8_sample(oracle, wl, kc, vc, s, scales):
     return oracle.quantize_kv(kb, "bf16", scales[0]), oracle.quantize_kv(vb, "bf16", scales[1]), table
 
 
-def _cpu_baseline(wl, budget_s: float = 12.0, fp8_scales=None):
-    """Time the oracle's attention on the batch's sequences, one at a time in
-    batch order (wrapping round to the first sequence after the last), until
-    about budget_s of work is done; report the KV GB/s of that sample (the
-    same bytes model as the GPU value).  With fp8_scales the oracle reads E4M3
-    pools (quantised per sequence outside the timed part)."""
-    import oracle
+# ----------------------------------------------------------------- the CPU leg
+# Everything below up to bench_blocks is the benchmark's CPU-baseline leg: the
+# only code here that runs the float64 oracle.  It times the oracle on the
+# host cores and keeps the rows it computed, which the GPU rows of the same
+# step are then compared with.
+
+def _host_info() -> dict:
+    model = ""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    return {"host_cpu_model": model, "host_cpu_count": os.cpu_count(), "host_affinity": affinity}
+
+
+def _pool_workers() -> int:
+    """Worker processes of the oracle pool: every core this process may run
+    on, at most 16 -- a one-GPU share of the host (the bench host gives one
+    GPU's jobs 16 cores, whatever os.cpu_count() reports)."""
+    return max(1, min(16, _host_info()["host_affinity"]))
+
+
+_POOL = {}                                       # inherited by the forked workers
+
+
+def _pool_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:
-        threads = 1
+        pass
+
+
+def _oracle_seq_rows(i: int):
+    """Oracle rows of sequence i of the step (its decode row, or its chunk's
+    rows), from the pools after the step's write."""
+    import oracle
+    st = _POOL
+    r0, r1 = int(st["qsl"][i]), int(st["qsl"][i + 1])
+    return oracle.varlen_attention(st["q"][r0:r1], st["kc"], st["vc"], st["bt"][i:i + 1], st["sl"][i:i + 1],
+                                   np.array([0, r1 - r0]), st["scale"], st["dtype"])
+
+
+def cpu_baseline_pool(wl, budget_s: float = 12.0) -> tuple:
+    """The oracle's attention for every sequence of the step (after the step's
+    cache write), one sequence per task on a fork-started process pool with
+    BLAS at one thread per worker, repeated over the batch until about
+    budget_s of wall time (at least one pass).  Must run before the GPU is
+    initialised (the workers are forked).  Returns (record, the oracle's rows
+    of the first pass [T, Hq, D])."""
+    import multiprocessing as mp
+    import oracle
     slots = oracle.slot_mapping(wl.block_tables, wl.positions, wl.query_start_loc, wl.spec.block_size)
     kc, vc = oracle.reshape_and_cache(wl.key, wl.value, wl.key_cache, wl.value_cache, slots)
-    decode = not wl.is_prefill.any()
-    dt = 0.0
-    done, tokens, rows = 0, 0, 0
-    while dt < budget_s:
-        i = done % wl.num_seqs
-        s = slice(i, i + 1)
-        r0, r1 = int(wl.query_start_loc[i]), int(wl.query_start_loc[i + 1])
-        pk, pv, table, dts = kc, vc, wl.block_tables[s], wl.spec.dtype
-        if fp8_scales is not None:
-            pk, pv, table = _fp8_sample(oracle, wl, kc, vc, i, fp8_scales)
+    _POOL.update(q=wl.query, kc=kc, vc=vc, bt=wl.block_tables, sl=wl.seq_lens, qsl=wl.query_start_loc,
+                 scale=wl.scale, dtype=wl.spec.dtype)
+    B = wl.num_seqs
+    # one worker: sequences in batch order for about 3 s (the single-core rate)
+    t0 = time.perf_counter()
+    n1 = r1 = tok1 = 0
+    while n1 < B and time.perf_counter() - t0 < 3.0:
+        r1 += int(wl.query_lens[n1])
+        tok1 += int(wl.seq_lens[n1])
+        _oracle_seq_rows(n1)
+        n1 += 1
+    single = time.perf_counter() - t0
+    workers = _pool_workers()
+    passes = 0
+    with mp.get_context("fork").Pool(workers, initializer=_pool_init) as pool:
+        pool.map(_oracle_seq_rows, range(min(B, workers)), chunksize=1)          # start-up, untimed
         t0 = time.perf_counter()
-        if decode:
-            oracle.decode_attention(wl.query[r0:r1], pk, pv, table, wl.seq_lens[s], wl.scale, dts, fp8_scales)
-        else:
-            oracle.varlen_attention(wl.query[r0:r1], pk, pv, table, wl.seq_lens[s], np.array([0, r1 - r0]),
-                                    wl.scale, dts, fp8_scales)
-        dt += time.perf_counter() - t0
-        tokens += int(wl.seq_lens[i])
-        rows += r1 - r0
-        done += 1
+        first = None
+        while True:
+            res = pool.map(_oracle_seq_rows, range(B), chunksize=1)
+            if first is None:
+                first = np.concatenate(res)
+            passes += 1
+            wall = time.perf_counter() - t0
+            if wall >= budget_s:
+                break
+    _POOL.clear()
     sp = wl.spec
-    nbytes = tokens * 2 * sp.num_kv_heads * sp.head_dim * (1 if fp8_scales is not None else wl.elem_bytes)
-    passes, extra = divmod(done, wl.num_seqs)
-    covered = ("%d full pass%s over the %d sequences%s" % (passes, "" if passes == 1 else "es", wl.num_seqs,
-                                                          " plus the first %d" % extra if extra else "")
-               if passes else "the first %d of %d sequences" % (done, wl.num_seqs))
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": "float64 NumPy oracle %s%s attention, %s (%d query rows, %d KV tokens), %.1f s"
-                      % ("E4M3 " if fp8_scales else "", "decode" if decode else "varlen", covered, rows, tokens, dt),
-            "seq_tokens_per_s": round(rows / dt, 3)}
+    per_tok = 2 * sp.num_kv_heads * sp.head_dim * wl.elem_bytes
+    pass_bytes = int(wl.seq_lens.astype(np.int64).sum()) * per_tok
+    host = _host_info()
+    rec = {"value": round(passes * pass_bytes / wall / 1e9, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
+           "sample": "float64 NumPy oracle attention over the whole step (%d sequences, %d query rows, after the "
+                     "step's cache write), %d pass%s, one sequence per task on %d worker processes (fork, BLAS "
+                     "1 thread each), %.1f s wall" % (B, wl.num_tokens, passes, "" if passes == 1 else "es", workers,
+                                                      wall),
+           "seq_tokens_per_s": round(passes * wl.num_tokens / wall, 2),
+           "single_worker": {"value": round(tok1 * per_tok / single / 1e9, 4), "unit": "GB/s",
+                             "seq_tokens_per_s": round(r1 / single, 2), "sequences": n1, "wall_s": round(single, 3)},
+           "workers": workers, **host}
+    return rec, first
+
+
+def oracle_sample(wl, seqs, fp8_scales=None) -> tuple:
+    """Oracle rows of the given sequences (in-process, one core): decode rows
+    for decode workloads, each sequence's rows of the varlen step otherwise.
+    Returns (rows [n_rows, Hq, D] float64, the GPU row indices they match,
+    wall seconds, query rows, KV tokens)."""
+    import oracle
+    slots = oracle.slot_mapping(wl.block_tables, wl.positions, wl.query_start_loc, wl.spec.block_size)
+    kc, vc = oracle.reshape_and_cache(wl.key, wl.value, wl.key_cache, wl.value_cache, slots)
+    outs, rows = [], []
+    tokens = 0
+    t0 = time.perf_counter()
+    for s in seqs:
+        r0, r1 = int(wl.query_start_loc[s]), int(wl.query_start_loc[s + 1])
+        pk, pv, table, dt = kc, vc, wl.block_tables[s:s + 1], wl.spec.dtype
+        q = wl.query[r0:r1]
+        if fp8_scales is not None:
+            pk, pv, table = _fp8_sample(oracle, wl, kc, vc, s, fp8_scales)
+        outs.append(oracle.varlen_attention(q, pk, pv, table, wl.seq_lens[s:s + 1], np.array([0, r1 - r0]),
+                                            wl.scale, dt, fp8_scales))
+        rows.extend(range(r0, r1))
+        tokens += int(wl.seq_lens[s])
+    wall = time.perf_counter() - t0
+    return np.concatenate(outs), np.array(rows), wall, len(rows), tokens
+
+
+def errors(got: np.ndarray, ref: np.ndarray) -> dict:
+    d = got.astype(np.float64) - ref
+    n = float(np.linalg.norm(ref))
+    return {"max_abs_err": float(np.abs(d).max()) if d.size else 0.0,
+            "rel_l2_err": float(np.linalg.norm(d) / n) if n > 0 else float(np.linalg.norm(d)),
+            "finite": bool(np.isfinite(got).all())}
 
 
 def bench_blocks(args) -> int:
@@ -305,13 +402,259 @@ def bench_serve(args) -> int:
     return 0
 
 
+def _sample_seqs(wl, n: int = 8):
+    """Sequences whose rows the oracle recomputes for the error check: every
+    prefill chunk's sequence (at most two, the longest contexts first) and up
+    to n decode sequences spread over the batch, the longest included."""
+    pre = [int(s) for s in np.where(wl.is_prefill)[0]]
+    pre = sorted(pre, key=lambda s: -int(wl.seq_lens[s]))[:2]
+    dec = [int(s) for s in np.where(~wl.is_prefill)[0]]
+    pick = set()
+    if dec:
+        pick.add(max(dec, key=lambda s: int(wl.seq_lens[s])))
+        for i in np.linspace(0, len(dec) - 1, num=min(n, len(dec))).astype(int):
+            pick.add(dec[int(i)])
+    return pre + sorted(pick)[:n]
+
+
+class GpuCase:
+    """One workload resident on the GPU, with its step function."""
+
+    def __init__(self, cfg: int, fp8: bool, two_call: bool, wl=None):
+        import torch
+        from paged_kv_cache_97_amd import ops
+        from paged_kv_cache_97_amd import workloads as W
+        self.torch, self.ops = torch, ops
+        dev = torch.device("cuda:0")
+        self.wl = wl = W.generate(cfg) if wl is None else wl
+        self.cfg, self.fp8 = cfg, fp8
+        sp = wl.spec
+        print("bench: config %d%s (%s) B=%d sum(seq_len)=%d generated" % (
+            cfg, " E4M3" if fp8 else "", sp.name, wl.num_seqs, int(wl.seq_lens.sum())), file=sys.stderr, flush=True)
+
+        def up(a):
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to(dev)
+
+        q, key, value = up(wl.query), up(wl.key), up(wl.value)
+        kc, vc = up(wl.key_cache), up(wl.value_cache)
+        if fp8:
+            if sp.dtype != "bf16":
+                raise SystemExit("bench.py: --kv-cache-dtype fp8 needs a bf16 workload")
+            # E4M3 pools, filled from the resident bf16 pools by the library's
+            # own quantising write (every slot; free slots hold garbage codes,
+            # as reused blocks would)
+            nb_slots = kc.shape[0] * kc.shape[1]
+            kc8 = torch.empty(kc.shape, dtype=torch.uint8, device=dev)
+            vc8 = torch.empty(vc.shape, dtype=torch.uint8, device=dev)
+            ops.reshape_and_cache_fp8(kc.view(nb_slots, sp.num_kv_heads, sp.head_dim),
+                                      vc.view(nb_slots, sp.num_kv_heads, sp.head_dim), kc8, vc8,
+                                      torch.arange(nb_slots, dtype=torch.int64, device=dev), FP8_K_SCALE,
+                                      FP8_V_SCALE)
+            torch.cuda.synchronize()
+            del kc, vc
+            kc, vc = kc8, vc8
+        bt, sl, pos, qsl = up(wl.block_tables), up(wl.seq_lens), up(wl.positions), up(wl.query_start_loc)
+        slots = torch.empty(wl.num_tokens, dtype=torch.int64, device=dev)
+        self.out = out = torch.empty(wl.num_tokens, sp.num_q_heads, sp.head_dim, dtype=torch.float32, device=dev)
+        self.varlen = varlen = bool(wl.is_prefill.any())
+        ws = torch.empty(ops.varlen_workspace_size(wl.num_seqs, wl.num_tokens, sp.num_q_heads, sp.num_kv_heads,
+                                                   sp.head_dim, wl.max_query_len, sp.block_size, q.dtype),
+                         dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        self.fused = fused = not varlen and not two_call
+        self.tensors = (q, key, value, kc, vc, bt, sl, pos, qsl, slots, ws)
+
+        def step():
+            if fused:
+                # one call: the new tokens' slot mapping and cache write run
+                # inside the decode attention launch
+                if fp8:
+                    ops.decode_step_fp8(q, key, value, kc, vc, bt, sl, wl.scale, wl.max_seq_len, FP8_K_SCALE,
+                                        FP8_V_SCALE, out=out, workspace=ws)
+                else:
+                    ops.decode_step(q, key, value, kc, vc, bt, sl, wl.scale, wl.max_seq_len, out=out, workspace=ws)
+                return
+            if fp8:
+                ops.write_new_tokens_fp8(bt, pos, qsl, sp.block_size, key, value, kc, vc, FP8_K_SCALE, FP8_V_SCALE,
+                                         slots)
+                if varlen:
+                    ops.paged_attention_varlen_fp8(q, kc, vc, bt, sl, qsl, wl.scale, wl.max_query_len,
+                                                   wl.max_seq_len, FP8_K_SCALE, FP8_V_SCALE, out=out, workspace=ws)
+                else:
+                    ops.paged_attention_decode_fp8(q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, FP8_K_SCALE,
+                                                   FP8_V_SCALE, out=out, workspace=ws)
+                return
+            # slot mapping + cache write of the step's new tokens (one fused kernel)
+            ops.write_new_tokens(bt, pos, qsl, sp.block_size, key, value, kc, vc, slots)
+            if varlen:
+                ops.paged_attention_varlen(q, kc, vc, bt, sl, qsl, wl.scale, wl.max_query_len, wl.max_seq_len,
+                                           out=out, workspace=ws)
+            else:
+                ops.paged_attention_decode(q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, out=out, workspace=ws)
+
+        self.step = step
+
+    # bytes and flops of one step
+    def kv_bytes(self) -> int:
+        return self.wl.kv_bytes_logical() // (2 if self.fp8 else 1)
+
+    def kv_bytes_unique(self) -> int:
+        return self.wl.kv_bytes_unique() // (2 if self.fp8 else 1)
+
+    def step_name(self) -> str:
+        f = "_fp8" if self.fp8 else ""
+        if self.fused:
+            return "decode_step%s (slot mapping + reshape_and_cache fused into paged decode attention)" % f
+        return "write_new_tokens%s (slot mapping + reshape_and_cache) + paged_attention_%s%s" % (
+            f, "varlen" if self.varlen else "decode", f)
+
+    def kernel_name(self) -> str:
+        return "prefill_kernel" if self.varlen else "decode_split_kernel"
+
+    def warmup(self, n: int):
+        for _ in range(n):
+            self.step()
+        self.torch.cuda.synchronize()
+
+    def time_back_to_back(self, n: int) -> float:
+        """Mean ms per step of n whole steps between two stream events, with
+        nothing else recorded (the contract's timing)."""
+        torch = self.torch
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(n):
+            self.step()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n
+
+    def time_kernel(self, n: int) -> list:
+        """Per-launch ms of the dominant kernel (split kernel for decode, prefill
+        kernel for varlen), from HIP events the library records on its stream
+        right before and after it."""
+        ops = self.ops
+        evs = [(ops.HipEvent(), ops.HipEvent()) for _ in range(n)]
+        self.torch.cuda.synchronize()
+        for e0, e1 in evs:
+            ops.set_profile_events(e0, e1)
+            self.step()
+        ops.set_profile_events(None, None)
+        self.torch.cuda.synchronize()
+        return [ops.HipEvent.elapsed_ms(e0, e1) for e0, e1 in evs]
+
+    def time_each(self, n: int, flush=None) -> list:
+        """ms of each step alone: stream events right around it, after an
+        optional flush enqueued outside the events."""
+        torch = self.torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            if flush is not None:
+                flush()
+            e0.record()
+            self.step()
+            e1.record()
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+    def rows(self, idx) -> np.ndarray:
+        return self.out[self.torch.from_numpy(np.asarray(idx, dtype=np.int64)).to(self.out.device)].cpu().numpy()
+
+
+def _dist(ms: list) -> dict:
+    return {"median": round(float(np.median(ms)), 5), "min": round(float(np.min(ms)), 5),
+            "p90": round(float(np.percentile(ms, 90)), 5), "mean": round(float(np.mean(ms)), 5)}
+
+
+def _roofline(case: GpuCase, kern_ms: list) -> dict:
+    k_mean = float(np.mean(kern_ms))
+    if case.varlen:
+        flops = prefill_flops(case.wl)
+        achieved = flops / (k_mean * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": case.kernel_name(), "achieved": round(achieved, 2),
+                "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_TFLOPS, 4),
+                "traffic": None, "kernel_ms_mean": round(k_mean, 5),
+                "kernel_ms_min": round(float(np.min(kern_ms)), 5), "flops_per_launch": flops}
+    kvb = case.kv_bytes()
+    achieved = kvb / (k_mean * 1e-3) / 1e9
+    tr = _load_traffic() if case.cfg == 3 and not case.fp8 else None
+    return {"bound": "hbm", "kernel": case.kernel_name(), "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": round(tr["traffic_bytes_per_launch"]) if tr else None,
+            "kernel_ms_mean": round(k_mean, 5), "kernel_ms_min": round(float(np.min(kern_ms)), 5),
+            "bytes_per_launch": kvb}
+
+
+def config_record(case: GpuCase, ms_step: float, each_ms: list, kern_ms: list, check: dict) -> dict:
+    """The per-workload summary the suite line carries."""
+    wl, sp = case.wl, case.wl.spec
+    kvb = case.kv_bytes()
+    rec = {"workload": sp.name + (" (E4M3 pools)" if case.fp8 else ""), "seed": wl.seed,
+           "num_seqs": wl.num_seqs, "query_rows": wl.num_tokens, "sum_seq_len": int(wl.seq_lens.sum()),
+           "kv_cache_dtype": "fp8-e4m3" if case.fp8 else sp.dtype, "step": case.step_name(),
+           "ms_per_step": round(ms_step, 5), "step_ms": _dist(each_ms),
+           "kv_bytes": kvb, "kv_GBps": round(kvb / (ms_step * 1e-3) / 1e9, 2),
+           "pct_of_hbm_peak": round(100.0 * kvb / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+           "seq_tokens_per_s": round(wl.num_tokens / (ms_step * 1e-3), 1),
+           "kv_tokens_per_s": round(float(wl.seq_lens.sum()) / (ms_step * 1e-3), 1),
+           "roofline": _roofline(case, kern_ms), "oracle_check": check}
+    if sp.shared_prefix_tokens:
+        u = case.kv_bytes_unique()
+        rec["kv_bytes_unique"] = u
+        rec["pct_of_hbm_peak_unique"] = round(100.0 * u / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)
+        rec["roofline"]["frac_unique"] = round(u / (float(np.mean(kern_ms)) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+    if case.varlen:
+        rec["decode_rows"] = int((~wl.is_prefill).sum())
+        rec["prefill_rows"] = int(wl.query_lens[wl.is_prefill].sum())
+        rec["prefill_flops"] = prefill_flops(wl)
+        rec["prefill_TFLOPs_at_step"] = round(prefill_flops(wl) / (ms_step * 1e-3) / 1e12, 1)
+    return rec
+
+
+def check_against_oracle(case: GpuCase, ref_rows=None) -> dict:
+    """Errors of the GPU rows of the last step against the oracle's rows of the
+    same step: the whole batch when ref_rows (the CPU baseline's first pass)
+    is given, else a sample of sequences recomputed here."""
+    wl = case.wl
+    if ref_rows is not None:
+        idx = np.arange(wl.num_tokens)
+        e = errors(case.rows(idx), ref_rows)
+        e.update({"rows": int(len(idx)), "sample": "every row of the step (the CPU baseline's first pass)"})
+        return e
+    seqs = _sample_seqs(wl)
+    ref, idx, wall, nrows, tokens = oracle_sample(wl, seqs, (FP8_K_SCALE, FP8_V_SCALE) if case.fp8 else None)
+    e = errors(case.rows(idx), ref)
+    e.update({"rows": int(nrows), "sample": "%d sequences (%d query rows, %d KV tokens): %s" % (
+        len(seqs), nrows, tokens, ",".join(map(str, seqs))), "oracle_wall_s": round(wall, 3),
+        "oracle_cores": 1})
+    return e
+
+
+def bench_case(case: GpuCase, args, ref_rows=None, check=True) -> tuple:
+    case.warmup(args.warmup)
+    ms_step = case.time_back_to_back(args.steps)
+    kern_ms = case.time_kernel(args.steps)
+    each_ms = case.time_each(args.steps)
+    chk = check_against_oracle(case, ref_rows) if check else None
+    print("bench: %.4f ms/step, %s mean %.4f ms (min %.4f, p90 %.4f)" % (
+        ms_step, case.kernel_name(), float(np.mean(kern_ms)), float(np.min(kern_ms)),
+        float(np.percentile(kern_ms, 90))), file=sys.stderr, flush=True)
+    return ms_step, kern_ms, each_ms, chk
+
+
+SUITE = [("1", 1, False), ("2", 2, False), ("3-e4m3", 3, True), ("4", 4, False), ("5", 5, False)]
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--config", type=int, default=None,
+                    help="run only this workload (default: workload 3 as the headline, then the others)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline and the oracle checks")
     ap.add_argument("--kernels-only", action="store_true",
                     help="run warmup + steps untimed, then one plain %d MiB device copy (counter runs)" % (CALIB_BYTES >> 20))
     ap.add_argument("--summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -330,7 +673,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.summarize:
         from paged_kv_cache_97_amd import workloads as W
-        wl = W.generate(args.config)
+        wl = W.generate(args.config or 3)
         rec = summarize(args.summarize[0], args.summarize[1], wl.kv_bytes_logical(), args.command)
         os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
         with open(TRAFFIC_FILE, "w") as f:
@@ -343,89 +686,33 @@ def main() -> int:
         return 2
 
     import torch
-    from paged_kv_cache_97_amd import ops
     from paged_kv_cache_97_amd import workloads as W
 
+    suite = args.config is None
+    cfg = 3 if suite else args.config
+    fp8 = args.kv_cache_dtype == "fp8"
+    wl = W.generate(cfg)
+    # The CPU baseline forks its worker pool, so it runs before anything
+    # touches the GPU; its first pass is the oracle's answer for every row.
+    cpu, ref_rows = None, None
+    if not args.no_cpu and not args.kernels_only and not fp8:
+        cpu, ref_rows = cpu_baseline_pool(wl)
+        print("bench: CPU oracle baseline %.3f GB/s on %d workers" % (cpu["value"], cpu["cores"]),
+              file=sys.stderr, flush=True)
+
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from paged_kv_cache_97_amd import ops
+    ops.lib()
     if args.blocks:
         return bench_blocks(args)
     if args.serve:
         return bench_serve(args)
     dev = torch.device("cuda:0")
-    ops.lib()
-    wl = W.generate(args.config)
-    sp = wl.spec
-    print("bench: config %d (%s) B=%d sum(seq_len)=%d generated" % (args.config, sp.name, wl.num_seqs,
-          int(wl.seq_lens.sum())), file=sys.stderr, flush=True)
-
-    def up(a):
-        t = torch.from_numpy(np.ascontiguousarray(a))
-        return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to(dev)
-
-    q, key, value = up(wl.query), up(wl.key), up(wl.value)
-    kc, vc = up(wl.key_cache), up(wl.value_cache)
-    fp8 = args.kv_cache_dtype == "fp8"
-    if fp8:
-        if sp.dtype != "bf16":
-            print("bench.py: --kv-cache-dtype fp8 needs a bf16 workload", file=sys.stderr)
-            return 2
-        # E4M3 pools, filled from the resident bf16 pools by the library's own
-        # quantising write (every slot; free slots hold garbage codes, as reused
-        # blocks would)
-        nb_slots = kc.shape[0] * kc.shape[1]
-        kc8 = torch.empty(kc.shape, dtype=torch.uint8, device=dev)
-        vc8 = torch.empty(vc.shape, dtype=torch.uint8, device=dev)
-        ops.reshape_and_cache_fp8(kc.view(nb_slots, sp.num_kv_heads, sp.head_dim),
-                                  vc.view(nb_slots, sp.num_kv_heads, sp.head_dim), kc8, vc8,
-                                  torch.arange(nb_slots, dtype=torch.int64, device=dev), FP8_K_SCALE, FP8_V_SCALE)
-        torch.cuda.synchronize()
-        del kc, vc
-        kc, vc = kc8, vc8
-    bt, sl, pos, qsl = up(wl.block_tables), up(wl.seq_lens), up(wl.positions), up(wl.query_start_loc)
-    slots = torch.empty(wl.num_tokens, dtype=torch.int64, device=dev)
-    out = torch.empty(wl.num_tokens, sp.num_q_heads, sp.head_dim, dtype=torch.float32, device=dev)
-    varlen = bool(wl.is_prefill.any())
-    ws = torch.empty(ops.varlen_workspace_size(wl.num_seqs, wl.num_tokens, sp.num_q_heads, sp.num_kv_heads,
-                                               sp.head_dim, wl.max_query_len, sp.block_size, q.dtype),
-                     dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-
-    fused = not varlen and not args.two_call
-
-    def step():
-        if fused:
-            # one call: the new tokens' slot mapping and cache write run inside
-            # the decode attention launch
-            if fp8:
-                ops.decode_step_fp8(q, key, value, kc, vc, bt, sl, wl.scale, wl.max_seq_len, FP8_K_SCALE,
-                                    FP8_V_SCALE, out=out, workspace=ws)
-            else:
-                ops.decode_step(q, key, value, kc, vc, bt, sl, wl.scale, wl.max_seq_len, out=out, workspace=ws)
-            return
-        if fp8:
-            ops.write_new_tokens_fp8(bt, pos, qsl, sp.block_size, key, value, kc, vc, FP8_K_SCALE, FP8_V_SCALE,
-                                     slots)
-            if varlen:
-                ops.paged_attention_varlen_fp8(q, kc, vc, bt, sl, qsl, wl.scale, wl.max_query_len, wl.max_seq_len,
-                                               FP8_K_SCALE, FP8_V_SCALE, out=out, workspace=ws)
-            else:
-                ops.paged_attention_decode_fp8(q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, FP8_K_SCALE, FP8_V_SCALE,
-                                               out=out, workspace=ws)
-            return
-        # slot mapping + cache write of the step's new tokens (one fused kernel)
-        ops.write_new_tokens(bt, pos, qsl, sp.block_size, key, value, kc, vc, slots)
-        if varlen:
-            ops.paged_attention_varlen(q, kc, vc, bt, sl, qsl, wl.scale, wl.max_query_len, wl.max_seq_len,
-                                       out=out, workspace=ws)
-        else:
-            ops.paged_attention_decode(q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, out=out, workspace=ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    case = GpuCase(cfg, fp8, args.two_call, wl)
     if args.kernels_only:
+        case.warmup(args.warmup)
         for _ in range(args.steps):
-            step()
+            case.step()
         a = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
         a.fill_(1)
         b = torch.empty_like(a)
@@ -435,43 +722,15 @@ def main() -> int:
               file=sys.stderr, flush=True)
         return 0
 
-    # Region A (the contract): K whole steps between two stream events, with
-    # nothing else recorded, so the step time carries no profiling markers.
-    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for _ in range(args.steps):
-        step()
-    t_stop.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_stop)
-    # Region B: the same K steps again, now with HIP events that the library
-    # records on its stream right before and after the dominant kernel (split
-    # kernel for decode, prefill kernel for varlen), giving its duration per
-    # launch.
-    evs = [(ops.HipEvent(), ops.HipEvent()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for e0, e1 in evs:
-        ops.set_profile_events(e0, e1)
-        step()
-    ops.set_profile_events(None, None)
-    torch.cuda.synchronize()
-    kern_ms = [ops.HipEvent.elapsed_ms(e0, e1) for e0, e1 in evs]
-    ms_step = total_ms / args.steps
-    # Region C: each step timed alone after the library's streaming read of
-    # 1 GiB of other data (outside its events, read-only so no dirty lines
-    # are left to write back), so neither the L2s nor the 256 MB last-level
-    # cache hold anything of the previous step.
+    ms_step, kern_ms, each_ms, chk = bench_case(case, args, ref_rows, check=not args.no_cpu)
+    # Each step alone after the library's streaming read of 1 GiB of other
+    # data (read-only, so no dirty lines are left to write back), and after
+    # an overwrite of 1 GiB (plain stores; the step then also pays for the
+    # write-back of what the overwrite left dirty in the caches).
     sink = torch.zeros(8192, dtype=torch.int32, device=dev)
     scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-    cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for e0, e1 in cold:
-        ops.stream_read(scratch, sink)
-        e0.record()
-        step()
-        e1.record()
-    torch.cuda.synchronize()
-    cold_ms = [e0.elapsed_time(e1) for e0, e1 in cold]
+    cold_ms = case.time_each(args.steps, lambda: ops.stream_read(scratch, sink))
+    cold_w_ms = case.time_each(args.steps, lambda: scratch.fill_(7))
     del scratch
     # The same streaming read over 4 GiB: the HBM read rate this part reaches
     # in practice, next to the 8 TB/s peak.
@@ -485,31 +744,16 @@ def main() -> int:
     torch.cuda.synchronize()
     stream_gbps = 10 * big.numel() * 4 / (r0.elapsed_time(r1) * 1e-3) / 1e9
     del big
-    kv_bytes = wl.kv_bytes_logical() // (2 if fp8 else 1)
+    head = config_record(case, ms_step, each_ms, kern_ms, chk)
+    kv_bytes = case.kv_bytes()
     value = kv_bytes / (ms_step * 1e-3) / 1e9
-    k_mean = float(np.mean(kern_ms))
-    kname = "prefill_kernel" if varlen else "decode_split_kernel"
-    print("bench: %.4f ms/step, %s mean %.4f ms (min %.4f, p90 %.4f)" % (
-        ms_step, kname, k_mean, float(np.min(kern_ms)), float(np.percentile(kern_ms, 90))),
-        file=sys.stderr, flush=True)
-    if varlen:
-        flops = prefill_flops(wl)
-        achieved = flops / (k_mean * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 2), "peak": MFMA_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_TFLOPS, 4), "traffic": None,
-                "kernel_ms_mean": round(k_mean, 5), "kernel_ms_min": round(float(np.min(kern_ms)), 5),
-                "flops_per_launch": flops}
-    else:
-        achieved = kv_bytes / (k_mean * 1e-3) / 1e9
-        tr = _load_traffic() if args.config == 3 and not fp8 else None
-        roof = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": round(tr["traffic_bytes_per_launch"]) if tr else None,
-                "kernel_ms_mean": round(k_mean, 5), "kernel_ms_min": round(float(np.min(kern_ms)), 5),
-                "bytes_per_launch": kv_bytes}
-    cpu = None
-    if not args.no_cpu:
-        cpu = _cpu_baseline(wl, fp8_scales=(FP8_K_SCALE, FP8_V_SCALE) if fp8 else None)
+    sp = wl.spec
+
+    def cold(ms, how):
+        return {**{k: v for k, v in _dist(ms).items() if k != "mean"},
+                "value_at_median": round(kv_bytes / (float(np.median(ms)) * 1e-3) / 1e9, 2),
+                "pct_at_median": round(100.0 * kv_bytes / (float(np.median(ms)) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                "how": how}
 
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -520,22 +764,30 @@ def main() -> int:
                    "num_kv_heads": sp.num_kv_heads, "head_dim": sp.head_dim, "block_size": sp.block_size,
                    "sum_seq_len": int(wl.seq_lens.sum()), "max_seq_len": wl.max_seq_len, "seed": wl.seed,
                    "kv_cache_dtype": "fp8 (E4M3, k/v scales %g/%g)" % (FP8_K_SCALE, FP8_V_SCALE) if fp8
-                   else sp.dtype,
-                   "step": ("decode_step%s (slot mapping + reshape_and_cache fused into paged decode attention)"
-                            % ("_fp8" if fp8 else "")) if fused else
-                           ("write_new_tokens%s (slot mapping + reshape_and_cache) + paged_attention_%s%s"
-                            % ("_fp8" if fp8 else "", "varlen" if varlen else "decode", "_fp8" if fp8 else ""))},
+                   else sp.dtype, "step": case.step_name()},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "seq_tokens_per_s": round(wl.num_tokens / (ms_step * 1e-3), 1),
         "kv_tokens_per_s": round(float(wl.seq_lens.sum()) / (ms_step * 1e-3), 1),
-        "roofline": roof,
+        "step_ms": _dist(each_ms),
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
-        "cold_step_ms": {"median": round(float(np.median(cold_ms)), 5), "min": round(float(np.min(cold_ms)), 5),
-                         "p90": round(float(np.percentile(cold_ms, 90)), 5),
-                         "value_at_median": round(kv_bytes / (float(np.median(cold_ms)) * 1e-3) / 1e9, 2),
-                         "how": "each step alone, after a streaming read of 1 GiB of other data (caches cold)"},
+        "oracle_check": chk,
+        "cold_step_ms": cold(cold_ms, "each step alone, after a streaming read of 1 GiB of other data"),
+        "cold_step_after_write_ms": cold(cold_w_ms, "each step alone, after 1 GiB of other data was overwritten "
+                                                    "with plain stores"),
         "hbm_stream_read_GBps": round(stream_gbps, 1),
     }
+    if suite:
+        del case
+        torch.cuda.empty_cache()
+        cfgs = {"3": head}
+        for key, c, f8 in SUITE:
+            other = GpuCase(c, f8, False, wl if (c == 3) else None)
+            o_ms, o_kern, o_each, o_chk = bench_case(other, args, None, check=not args.no_cpu)
+            cfgs[key] = config_record(other, o_ms, o_each, o_kern, o_chk)
+            del other
+            torch.cuda.empty_cache()
+        rec["configs"] = cfgs
     print(json.dumps(rec), flush=True)
     return 0
 
