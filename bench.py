@@ -458,7 +458,7 @@ class GpuCase:
         slots = torch.empty(wl.num_tokens, dtype=torch.int64, device=dev)
         self.out = out = torch.empty(wl.num_tokens, sp.num_q_heads, sp.head_dim, dtype=torch.float32, device=dev)
         self.varlen = varlen = bool(wl.is_prefill.any())
-        ws = torch.empty(ops.varlen_workspace_size(wl.num_seqs, wl.num_tokens, sp.num_q_heads, sp.num_kv_heads,
+        ws = torch.zeros(ops.varlen_workspace_size(wl.num_seqs, wl.num_tokens, sp.num_q_heads, sp.num_kv_heads,
                                                    sp.head_dim, wl.max_query_len, sp.block_size, q.dtype),
                          dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()

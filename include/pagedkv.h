@@ -190,9 +190,15 @@ size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                workspace nor clamps seq_lens (seq_lens are only clamped to
  *                max_blocks_per_seq*block_size, as above), so a value below
  *                the true lengths changes nothing.
- *   workspace    >= pkv_decode_workspace_size(...) bytes, 256-byte aligned,
- *                contents ignored on entry.  Long sequences are split over
- *                several workers (split-K); a second kernel merges the parts.
+ *   workspace    >= pkv_decode_workspace_size(...) bytes, 256-byte aligned.
+ *                Its first 4 bytes must be zero before the first call that
+ *                uses it (zero-fill a new workspace once); every call leaves
+ *                them zero again, and the rest of it is scratch.  Long
+ *                sequences are split over several workers (split-K); the
+ *                last part of the work is handed out in units from a counter
+ *                in that first word, and a second kernel merges the parts
+ *                (and resets the counter).  Calls sharing a workspace must
+ *                be ordered (one stream).
  *   num_seqs <= 8192.
  */
 int pkv_paged_attention_decode(float* out, const void* query, const void* key_cache,
@@ -270,7 +276,8 @@ int pkv_decode_step_fp8(float* out, const void* query, const void* key, const vo
  * before anything is enqueued.  All calls on one device share that array:
  * calls that overlap on one device (other streams, other host threads
  * without ordering) race and give wrong results; calls in one stream are
- * ordered and safe.  Nothing in it needs clearing between calls.
+ * ordered and safe.  The array starts zero-filled and every call leaves its
+ * counter word zero, so nothing needs clearing between calls.
  */
 int pkv_paged_attention_decode_noalloc(float* out, const void* query, const void* key_cache,
                                        const void* value_cache, const int32_t* block_tables,
@@ -394,6 +401,16 @@ int pkv_swap_blocks(const void* src_key, const void* src_value, void* dst_key, v
  * chunks of streaming on MI355X).  0 splits by real chunks only.  Results
  * do not depend on it beyond float reordering.  Returns the previous value
  * (-1 for an out-of-range argument).
+ *
+ * pkv_set_decode_dynamic: the share (permille, 0..500) of the decode
+ * split's chunks that is handed out in units of at least unit_chunks chunks
+ * (1..4096, default 4) from a counter, to the wavefronts that finish their
+ * static range first (the rest is split in equal static ranges).  0 gives a
+ * fully static split; -1 (the default) chooses per call: 100 for E4M3
+ * pools, 120 when the call has at most one (sequence, KV head, head tile)
+ * pair per four workers, else 0.  Every unit's range is fixed by the call's
+ * arguments, so results do not depend on which wavefront ran it.  Returns
+ * the previous share (-2 for an out-of-range argument).
  */
 int pkv_set_profile_events(void* start_event, void* stop_event);
 
@@ -413,6 +430,7 @@ int pkv_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t sink_
 int pkv_set_decode_workers(int32_t workers);
 int pkv_set_waves_per_cu(int32_t waves);
 int pkv_set_decode_segment_cost(int32_t chunks);
+int pkv_set_decode_dynamic(int32_t permille, int32_t unit_chunks);
 int pkv_get_waves_per_cu(void);
 
 #ifdef __cplusplus

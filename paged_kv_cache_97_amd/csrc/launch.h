@@ -38,6 +38,11 @@ struct DecodeArgs {
   // range crosses into a new pair (and pays the new pair's block-table and
   // first-chunk latency) gets that many fewer real chunks.  0: plain split.
   int seg_chunks;
+  // Dynamic tail: the last dyn_permille / 1000 of the chunk space is cut into
+  // units of at least unit_chunks chunks that wavefronts take from *counter
+  // (zero on entry; the merge kernel resets it) after their static range.
+  int dyn_permille;
+  int unit_chunks;
   // Optional fused cache write (decode only, qsl == NULL): new_k / new_v
   // [B, Hkv, D] are the rows of each sequence's new token, position
   // seq_lens[s] - 1 (query element type: float32 for F32 pools, bfloat16
@@ -55,6 +60,7 @@ struct DecodeArgs {
   int prefill_max_tok;
   // workspace
   int* cum;                   // [B + 1] chunk prefix sums (written by the split kernel)
+  int* counter;               // the units taken so far (the workspace's first word)
   float* part_ml;             // [slots, tile_cols, 2]  (max, sum) in the log2 domain
   float* part_o;              // [slots, tile_cols, D]  unnormalised partial outputs
 };

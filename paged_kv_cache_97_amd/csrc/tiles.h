@@ -1,7 +1,8 @@
 // MFMA tile primitives shared by the decode and varlen kernels (gfx950).
 //
-// A "chunk" is 32 consecutive logical tokens of one KV head, held as two
-// 16-token sub-tiles.  With tokens on the M side of the MFMA tiles:
+// A "chunk" is CT consecutive logical tokens of one KV head (32, or 64 for
+// the wide E4M3 decode tile), held as CT / 16 sub-tiles of 16 tokens.  With
+// tokens on the M side of the MFMA tiles:
 //   S^T[token, col] = K[token, :] . Q[col, :]          (A operand = K rows)
 //   O^T[dim, col]  += V^T[dim, token] P^T[token, col]   (A operand = V rows)
 // so a lane owns column col = lane % 16 of every accumulator, and the S^T
@@ -23,6 +24,9 @@ template <int D_, int BS_>
 struct TileBf16 {
   static constexpr int D = D_;
   static constexpr int BS = BS_;
+  static constexpr int CT = 32;      // tokens per chunk
+  static constexpr int NSUB = 2;     // 16-token sub-tiles per chunk
+  static constexpr bool kStoresInPatch = false;  // the writer calls store_new after patch_new
   static constexpr bool kDoubleBuffer = true;
   static constexpr int kWavesPerEU = 2;
   static constexpr int KK = D / 32;   // K=32 slices of the QK contraction
@@ -172,6 +176,9 @@ template <int D_, int BS_>
 struct TileF32 {
   static constexpr int D = D_;
   static constexpr int BS = BS_;
+  static constexpr int CT = 32;      // tokens per chunk
+  static constexpr int NSUB = 2;     // 16-token sub-tiles per chunk
+  static constexpr bool kStoresInPatch = false;  // the writer calls store_new after patch_new
   static constexpr bool kDoubleBuffer = false;
   static constexpr int kWavesPerEU = D == 128 ? 1 : 2;  // fp32 D=128 needs > 256 VGPRs
   static constexpr int NQ = D / 16;   // float4 pieces of a row per lane
@@ -316,9 +323,12 @@ struct TileF32 {
 // v_scale into the final normalisation).
 //
 // QK contraction order: the dot product may visit dims in any order as long
-// as K and Q agree, so lane row-group c owns the contiguous dims
-// [c*D/4, (c+1)*D/4) of a K row (D/4 bytes: one or two 16-byte loads) and
-// k-step kk uses dims c*D/4 + 8kk .. +7 of both operands.
+// as K and Q agree.  Load j of a K row (16 bytes per lane) gives lane
+// row-group c the dims 64j + 16c .. +15, so each load instruction reads one
+// contiguous 64-byte run of each of 16 rows (the way the bf16 tile's K loads
+// do; a lane-contiguous 32-byte split would make two instructions each touch
+// every 128-byte row at alternate 16-byte pieces); k-step kk = 2j + hh uses
+// dims 64j + 16c + 8hh .. +7 of both operands.
 // V keeps the bf16 tile's layout (rows 4c + r, dims VW*i ..), at one byte per
 // element, and is widened before the same in-lane transpose.
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
@@ -332,11 +342,14 @@ template <int D_, int BS_>
 struct TileFp8 {
   static constexpr int D = D_;
   static constexpr int BS = BS_;
+  static constexpr int CT = 32;      // tokens per chunk
+  static constexpr int NSUB = 2;     // 16-token sub-tiles per chunk
+  static constexpr bool kStoresInPatch = false;  // the writer calls store_new after patch_new
   static constexpr bool kDoubleBuffer = true;
   static constexpr int kWavesPerEU = 2;
   static constexpr int KK = D / 32;   // bf16 MFMA k-steps of the QK contraction
   static constexpr int KB = D / 4;    // K bytes per lane and row
-  static constexpr int KV = KB / 16;  // 16-byte K loads per lane and row
+  static constexpr int KV = KB / 16;  // 16-byte K loads per lane and row (load j: dims 64j + 16c ..)
   static constexpr int VW = D / 16;   // V dims (bytes) per lane and row
   static constexpr int NDT = D / 16;
   typedef uint8_t Elem;
@@ -347,22 +360,25 @@ struct TileFp8 {
   struct Q { u32x4 q[KK]; };
   struct Buf { u32x4 k[2][KV]; VRaw v[2][4]; };
 
+  // dims of k-step kk held by row-group c (see the contraction order above)
+  static __device__ __forceinline__ int q_dim(int kk, int c) { return 64 * (kk >> 1) + 16 * c + 8 * (kk & 1); }
+
   static __device__ __forceinline__ void load_q(Q& q, const QElem* qb, int cols) {
     const int l = lane_id(), i = l & 15, c = l >> 4;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      q.q[kk] = (i < cols) ? ld16(qb + i * D + KB * c + 8 * kk) : u32x4{0, 0, 0, 0};
+      q.q[kk] = (i < cols) ? ld16(qb + i * D + q_dim(kk, c)) : u32x4{0, 0, 0, 0};
   }
 
   static __device__ __forceinline__ void load_q_col(Q& q, const QElem* colp, bool valid) {
     const int c = lane_id() >> 4;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) q.q[kk] = valid ? ld16(colp + KB * c + 8 * kk) : u32x4{0, 0, 0, 0};
+    for (int kk = 0; kk < KK; ++kk) q.q[kk] = valid ? ld16(colp + q_dim(kk, c)) : u32x4{0, 0, 0, 0};
   }
 
   static __device__ __forceinline__ int k_lane_off(int rs) {
     const int l = lane_id();
-    return (l & 15) * rs + KB * (l >> 4);
+    return (l & 15) * rs + 16 * (l >> 4);
   }
   static __device__ __forceinline__ int v_lane_off(int rs) {
     const int l = lane_id();
@@ -375,7 +391,7 @@ struct TileFp8 {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int j = 0; j < KV; ++j) b.k[u][j] = ld_v<u32x4, STREAM>(kp[u] + koff + 16 * j);
+      for (int j = 0; j < KV; ++j) b.k[u][j] = ld_v<u32x4, STREAM>(kp[u] + koff + 64 * j);
 #pragma unroll
       for (int r = 0; r < 4; ++r) b.v[u][r] = ld_v<VRaw, STREAM>(vp[u] + voff + r * rs);
     }
@@ -387,7 +403,7 @@ struct TileFp8 {
       s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        // 8 bytes = dims c*D/4 + 8kk .. +7 of this lane's K row
+        // 8 bytes = dims q_dim(kk, c) .. +7 of this lane's K row
         const uint32_t w0 = b.k[u][kk >> 1][2 * (kk & 1)];
         const uint32_t w1 = b.k[u][kk >> 1][2 * (kk & 1) + 1];
         const u32x4 a = {fp8x2_to_bf16x2(w0, false), fp8x2_to_bf16x2(w0, true), fp8x2_to_bf16x2(w1, false),
@@ -462,8 +478,8 @@ struct TileFp8 {
     if (i == t)
 #pragma unroll
       for (int j = 0; j < KV; ++j) {
-        const u32x2 lo = quant8_bf16(ld16(nk + KB * c + 16 * j), k_inv);
-        const u32x2 hi = quant8_bf16(ld16(nk + KB * c + 16 * j + 8), k_inv);
+        const u32x2 lo = quant8_bf16(ld16(nk + 64 * j + 16 * c), k_inv);
+        const u32x2 hi = quant8_bf16(ld16(nk + 64 * j + 16 * c + 8), k_inv);
         const u32x4 code = {lo[0], lo[1], hi[0], hi[1]};
         if (tn >= 16) b.k[1][j] = code; else b.k[0][j] = code;
       }
@@ -485,7 +501,7 @@ struct TileFp8 {
     const int t = tn & 15;
     if (i == t)
 #pragma unroll
-      for (int j = 0; j < KV; ++j) st16(kd + KB * c + 16 * j, tn >= 16 ? b.k[1][j] : b.k[0][j]);
+      for (int j = 0; j < KV; ++j) st16(kd + 64 * j + 16 * c, tn >= 16 ? b.k[1][j] : b.k[0][j]);
     if (c == (t >> 2)) {
       VRaw x = b.v[0][0];
 #pragma unroll
@@ -494,6 +510,141 @@ struct TileFp8 {
         for (int r = 0; r < 4; ++r)
           if (16 * u + 4 * c + r == tn) x = b.v[u][r];
       *reinterpret_cast<VRaw*>(vd + VW * i) = x;
+    }
+  }
+
+  static __device__ __forceinline__ int out_dim(int dt, int c, int r) { return VW * (4 * c + r) + dt; }
+};
+
+// ------------------------------------------------------------ wide fp8 tile
+// The decode kernel's E4M3 tile: 64-token chunks (four 16-token sub-tiles),
+// held raw in registers until they are used.  An E4M3 chunk of 64 tokens
+// takes the register bytes of a bf16 chunk of 32, so each wavefront keeps
+// the same number of pool bytes in flight as the bf16 kernel (two chunks of
+// 16 KB for D 128), where 32-token E4M3 chunks would keep half.  Operand
+// layouts, widening and the pool scales are those of TileFp8; the PV product
+// takes sub-tiles (0, 1) and (2, 3) as two k = 32 MFMA steps.
+template <int D_, int BS_>
+struct TileFp8W {
+  static constexpr int D = D_;
+  static constexpr int BS = BS_;
+  static constexpr int CT = 64;
+  static constexpr int NSUB = 4;
+  // patch_new also stores the new token's codes (from the values it just
+  // encoded): reading them back out of one of four sub-tiles would index the
+  // chunk buffer dynamically and push it to scratch memory.
+  static constexpr bool kStoresInPatch = true;
+  static constexpr bool kDoubleBuffer = true;
+  static constexpr int kWavesPerEU = 2;
+  typedef TileFp8<D_, BS_> Narrow;
+  static constexpr int KK = Narrow::KK, KB = Narrow::KB, KV = Narrow::KV, VW = Narrow::VW, NDT = Narrow::NDT;
+  typedef uint8_t Elem;
+  typedef uint16_t QElem;
+  typedef typename Narrow::VVec VVec;
+  typedef typename Narrow::VRaw VRaw;
+  typedef typename Narrow::Q Q;
+
+  struct Buf { u32x4 k[NSUB][KV]; VRaw v[NSUB][4]; };
+
+  static __device__ __forceinline__ void load_q(Q& q, const QElem* qb, int cols) { Narrow::load_q(q, qb, cols); }
+  static __device__ __forceinline__ void load_q_col(Q& q, const QElem* colp, bool valid) {
+    Narrow::load_q_col(q, colp, valid);
+  }
+  static __device__ __forceinline__ int k_lane_off(int rs) { return Narrow::k_lane_off(rs); }
+  static __device__ __forceinline__ int v_lane_off(int rs) { return Narrow::v_lane_off(rs); }
+
+  template <bool STREAM = true>
+  static __device__ __forceinline__ void load(Buf& b, const Elem* const kp[NSUB], const Elem* const vp[NSUB],
+                                              int koff, int voff, int rs) {
+#pragma unroll
+    for (int u = 0; u < NSUB; ++u) {
+#pragma unroll
+      for (int j = 0; j < KV; ++j) b.k[u][j] = ld_v<u32x4, STREAM>(kp[u] + koff + 64 * j);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b.v[u][r] = ld_v<VRaw, STREAM>(vp[u] + voff + r * rs);
+    }
+  }
+
+  static __device__ __forceinline__ void qk(const Buf& b, const Q& q, f32x4 s[NSUB]) {
+#pragma unroll
+    for (int u = 0; u < NSUB; ++u) {
+      s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint32_t w0 = b.k[u][kk >> 1][2 * (kk & 1)];
+        const uint32_t w1 = b.k[u][kk >> 1][2 * (kk & 1) + 1];
+        const u32x4 a = {fp8x2_to_bf16x2(w0, false), fp8x2_to_bf16x2(w0, true), fp8x2_to_bf16x2(w1, false),
+                         fp8x2_to_bf16x2(w1, true)};
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, q.q[kk]), s[u], 0, 0, 0);
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void zero_v_rows(Buf& b, int valid) {
+    const int c = lane_id() >> 4;
+#pragma unroll
+    for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b.v[u][r] = 16 * u + 4 * c + r >= valid ? VRaw{} : b.v[u][r];
+  }
+
+  // k-step g takes sub-tiles 2g and 2g + 1: its slot 4v + r is token
+  // 16(2g + v) + 4c + r, for P and for the transposed V alike.
+  static __device__ __forceinline__ void pv(const Buf& b, const float p[NSUB][4], f32x4 o[NDT]) {
+#pragma unroll
+    for (int g = 0; g < NSUB / 2; ++g) {
+      bf16x8 pb;
+#pragma unroll
+      for (int v = 0; v < 2; ++v)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pb[4 * v + r] = (__bf16)p[2 * g + v][r];
+      VVec w[2][4];
+#pragma unroll
+      for (int v = 0; v < 2; ++v)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[v][r] = Narrow::widen(b.v[2 * g + v][r]);
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) {
+        u32x4 a;
+        a[0] = Narrow::pick(w[0][0], w[0][1], t);
+        a[1] = Narrow::pick(w[0][2], w[0][3], t);
+        a[2] = Narrow::pick(w[1][0], w[1][1], t);
+        a[3] = Narrow::pick(w[1][2], w[1][3], t);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pb, o[t], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- the step's new token (tn in 0..63): encoded from its bfloat16 input
+  // rows exactly as the quantising cache write does, as in TileFp8, and
+  // stored at kd / vd (its slot) when they are not null.
+  static __device__ __forceinline__ void patch_new(Buf& b, int tn, const void* nkp, const void* nvp, float k_inv,
+                                                   float v_inv, Elem* kd, Elem* vd) {
+    const uint16_t* nk = static_cast<const uint16_t*>(nkp);
+    const uint16_t* nv = static_cast<const uint16_t*>(nvp);
+    const int l = lane_id_here(), i = l & 15, c = l >> 4;
+    const int t = tn & 15, su = tn >> 4;
+    if (i == t)
+#pragma unroll
+      for (int j = 0; j < KV; ++j) {
+        const u32x2 lo = quant8_bf16(ld16(nk + 64 * j + 16 * c), k_inv);
+        const u32x2 hi = quant8_bf16(ld16(nk + 64 * j + 16 * c + 8), k_inv);
+        const u32x4 code = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u) b.k[u][j] = u == su ? code : b.k[u][j];
+        if (kd != nullptr) st16(kd + 64 * j + 16 * c, code);
+      }
+    if (c == (t >> 2)) {
+      const VVec x = *reinterpret_cast<const VVec*>(nv + VW * i);
+      VRaw vq;
+      if constexpr (VW == 8) vq = quant8_bf16(x, v_inv);
+      else vq = quant4(bf16_lo(x[0]), bf16_hi(x[0]), bf16_lo(x[1]), bf16_hi(x[1]), v_inv);
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) b.v[u][r] = 16 * u + 4 * c + r == tn ? vq : b.v[u][r];
+      if (vd != nullptr) *reinterpret_cast<VRaw*>(vd + VW * i) = vq;
     }
   }
 

@@ -83,7 +83,7 @@ class Engine:
                                                  pool_kind)))
         if ws <= 0:
             raise ValueError("shape not supported by the library")
-        self._ws = torch.empty(ws, dtype=torch.uint8, device=self.dev)
+        self._ws = torch.zeros(ws, dtype=torch.uint8, device=self.dev)   # a new workspace starts zero-filled
         self._stage = [None, None]
         self._stage_done = [None, None]
         self._dstage = None

@@ -72,6 +72,7 @@ _SIGNATURES = {
     "pkv_set_decode_workers": (_c_i32, [_c_i32]),
     "pkv_set_waves_per_cu": (_c_i32, [_c_i32]),
     "pkv_set_decode_segment_cost": (_c_i32, [_c_i32]),
+    "pkv_set_decode_dynamic": (_c_i32, [_c_i32, _c_i32]),
     "pkv_get_waves_per_cu": (_c_i32, []),
 }
 
@@ -202,9 +203,10 @@ def varlen_workspace_size(num_seqs: int, num_tokens: int, num_q_heads: int, num_
 
 
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
-    # the library checks the size (PKV_EWORKSPACE); this only allocates a default
+    # the library checks the size (PKV_EWORKSPACE); this only allocates a
+    # default, zero-filled as a new workspace must be
     if workspace is None:
-        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
     return workspace
 
 
@@ -518,6 +520,13 @@ def set_decode_segment_cost(n: int) -> int:
     """Virtual chunks the decode split charges per (sequence, KV head) range;
     returns the previous value."""
     return int(lib().pkv_set_decode_segment_cost(int(n)))
+
+
+def set_decode_dynamic(permille: int, unit_chunks: int = 4) -> int:
+    """Share (permille) of the decode split handed out in units of at least
+    unit_chunks chunks to the wavefronts that finish first (-1: chosen per
+    call); returns the previous share."""
+    return int(lib().pkv_set_decode_dynamic(int(permille), int(unit_chunks)))
 
 
 def set_waves_per_cu(n: int) -> int:

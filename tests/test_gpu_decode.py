@@ -262,3 +262,48 @@ def test_segment_cost_splits(cost, workers, dev):
     finally:
         ops.set_decode_workers(prev_w)
         ops.set_decode_segment_cost(prev_c)
+
+
+@pytest.mark.parametrize("permille,unit", [(0, 4), (60, 1), (120, 4), (300, 2), (500, 64)])
+@pytest.mark.parametrize("workers", [0, 3, 333, 4096])
+def test_dynamic_tail_splits(permille, unit, workers, dev):
+    """The split whose last chunks are handed out in units from a counter:
+    every share (none .. half), unit size and worker count (fewer chunks than
+    workers included) matches the oracle; the E4M3 wide tile and a segment
+    cost go through the same ranges."""
+    prev_w = ops.set_decode_workers(workers)
+    prev_d = ops.set_decode_dynamic(permille, unit)
+    prev_c = ops.set_decode_segment_cost(3 if workers == 333 else 0)
+    try:
+        _check_full(W.generate(SMALL["gqa8-bs16"], seed=41), dev, "dyn=%d/%d workers=%d" % (permille, unit, workers))
+        spec = W.reduced(3, num_decode=12, decode_len=("fixed", (1, 2, 31, 32, 33, 64, 65, 100, 1, 700, 3, 40)))
+        _check_full(W.generate(spec, seed=42), dev, "edges dyn=%d/%d workers=%d" % (permille, unit, workers))
+    finally:
+        ops.set_decode_workers(prev_w)
+        ops.set_decode_dynamic(prev_d, 4)
+        ops.set_decode_segment_cost(prev_c)
+
+
+def test_dynamic_tail_is_deterministic_and_resets_its_counter(dev):
+    """The units are fixed ranges, so which wavefront takes which unit does not
+    change the result: repeated calls (through one workspace, which the merge
+    leaves with a zero counter) give bit-identical outputs, and a call after
+    calls of other shapes on the same workspace is still exact."""
+    wl = W.generate(3)
+    t = upload(wl, dev)
+    slots, out0 = run_step(wl, t)
+    ws = torch.zeros(ops.decode_workspace_size(wl.num_seqs, wl.spec.num_q_heads, wl.spec.num_kv_heads,
+                                               wl.spec.head_dim, wl.spec.block_size, torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
+    small = W.generate(SMALL["gqa8-bs16"], seed=43)
+    ts = upload(small, dev)
+    outs = []
+    for i in range(6):
+        outs.append(ops.paged_attention_decode(t["query"], t["key_cache"], t["value_cache"], t["block_tables"],
+                                               t["seq_lens"], wl.scale, wl.max_seq_len, workspace=ws).clone())
+        ops.paged_attention_decode(ts["query"], ts["key_cache"], ts["value_cache"], ts["block_tables"],
+                                   ts["seq_lens"], small.scale, small.max_seq_len, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32)[0]) == 0, "the unit counter is left non-zero"
+    for o in outs:
+        assert torch.equal(o.view(torch.int32), out0.view(torch.int32))
