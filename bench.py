@@ -465,7 +465,20 @@ class GpuCase:
         self.fused = fused = not varlen and not two_call
         self.tensors = (q, key, value, kc, vc, bt, sl, pos, qsl, slots, ws)
 
+        # sequences that share a prefix (held once in the pool) are named to
+        # the library, which then reads those blocks once per group
+        self.shared = shared = bool(sp.shared_prefix_tokens) and fused and not fp8
+        groups = torch.tensor([[0, wl.num_seqs, sp.shared_prefix_tokens]], dtype=torch.int32, device=dev)
+        if shared:
+            ws = torch.zeros(max(ws.numel(), ops.decode_shared_workspace_size(
+                wl.num_seqs, sp.num_q_heads, sp.num_kv_heads, sp.head_dim, sp.block_size, q.dtype, 1)),
+                dtype=torch.uint8, device=dev)
+
         def step():
+            if shared:
+                ops.decode_step_shared(q, key, value, kc, vc, bt, sl, wl.scale, wl.max_seq_len, groups, out=out,
+                                       workspace=ws)
+                return
             if fused:
                 # one call: the new tokens' slot mapping and cache write run
                 # inside the decode attention launch
@@ -504,6 +517,10 @@ class GpuCase:
 
     def step_name(self) -> str:
         f = "_fp8" if self.fp8 else ""
+        if self.shared:
+            return ("decode_step_shared (slot mapping + reshape_and_cache fused into paged decode attention; the "
+                    "%d-token shared prefix read once for all %d sequences)" % (self.wl.spec.shared_prefix_tokens,
+                                                                              self.wl.num_seqs))
         if self.fused:
             return "decode_step%s (slot mapping + reshape_and_cache fused into paged decode attention)" % f
         return "write_new_tokens%s (slot mapping + reshape_and_cache) + paged_attention_%s%s" % (
@@ -633,7 +650,10 @@ def check_against_oracle(case: GpuCase, ref_rows=None) -> dict:
 
 
 def bench_case(case: GpuCase, args, ref_rows=None, check=True) -> tuple:
-    case.warmup(args.warmup)
+    # The mixed step's MFMA-bound prefill runs about 10 % slower in its first
+    # tens of steps on a cold part than afterwards, so it gets at least 20
+    # untimed steps.
+    case.warmup(max(args.warmup, 20) if case.varlen else args.warmup)
     ms_step = case.time_back_to_back(args.steps)
     kern_ms = case.time_kernel(args.steps)
     each_ms = case.time_each(args.steps)

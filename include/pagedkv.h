@@ -263,6 +263,61 @@ int pkv_decode_step_fp8(float* out, const void* query, const void* key, const vo
                         float k_scale, float v_scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Shared prefixes (feifeigd.github.io "vLLM 架构详解" 一, 共享前缀的 Block
+ * 复用: sequences that start with the same tokens -- a system prompt, the
+ * prompt of parallel samples -- hold that prefix once, in physical blocks
+ * whose reference count exceeds one).  These calls compute exactly what
+ * pkv_paged_attention_decode / pkv_decode_step compute (the same results up
+ * to float summation order), but read each group's shared blocks once for
+ * all its members' query heads instead of once per member.
+ *   prefix_groups  int32 [num_groups][3] (device, read): for group g,
+ *                  (first_seq, num_seqs, shared_tokens): sequences first_seq
+ *                  .. first_seq + num_seqs - 1 share their first
+ *                  shared_tokens tokens, i.e. their block tables hold the
+ *                  same block ids for those tokens (the prefix is read
+ *                  through the table of first_seq).  Values are clamped to
+ *                  the batch and shared_tokens is rounded down to a multiple
+ *                  of 16 (the members read the rest through their own
+ *                  tables, which is still exact).  A member shorter than the
+ *                  prefix attends only its own seq_lens tokens.  Groups
+ *                  should not overlap (a sequence in two groups is still
+ *                  computed exactly, through one of them, with some work
+ *                  repeated).  Tables that do not agree on the shared blocks
+ *                  give unspecified (memory-safe) results.
+ *   num_groups     host scalar, 0 .. 1024 (0: the plain call).
+ *   pkv_decode_step_shared: as pkv_decode_step; a member's new token is
+ *                  never read from the shared blocks (a decode step does not
+ *                  write into a shared block: the host copies it first).
+ *   dtype PKV_BF16 (and E4M3 pools through the _fp8 call); num_seqs <= 4096.
+ *   workspace >= pkv_decode_shared_workspace_size(..., num_groups) bytes,
+ *   256-byte aligned, first 4 bytes zero before its first use (as for
+ *   pkv_paged_attention_decode); PKV_EUNSUPPORTED for float32 pools.
+ */
+size_t pkv_decode_shared_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, pkv_dtype dtype, int32_t num_groups);
+int pkv_paged_attention_decode_shared(float* out, const void* query, const void* key_cache,
+                                      const void* value_cache, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
+                                      pkv_dtype dtype, const int32_t* prefix_groups, int32_t num_groups,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+int pkv_paged_attention_decode_shared_fp8(float* out, const void* query, const void* key_cache,
+                                          const void* value_cache, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                          int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
+                                          float k_scale, float v_scale, const int32_t* prefix_groups,
+                                          int32_t num_groups, void* workspace, size_t workspace_bytes,
+                                          void* stream);
+int pkv_decode_step_shared(float* out, const void* query, const void* key, const void* value, void* key_cache,
+                           void* value_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t max_seq_len,
+                           float scale, pkv_dtype dtype, const int32_t* prefix_groups, int32_t num_groups,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Allocation-free decode attention, for callers that cannot allocate device
  * memory or pass a workspace: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  Same computation, arguments (less

@@ -420,16 +420,19 @@ static int run_decode(float* out, const void* query, const void* key_cache, cons
                       int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t max_seq_len,
                       float scale, KvFormat fmt, void* workspace, size_t workspace_bytes,
                       hipStream_t stream, const void* new_k = nullptr, const void* new_v = nullptr,
-                      int* prefill_plan = nullptr) {
+                      int* prefill_plan = nullptr, const int32_t* groups = nullptr, int num_groups = 0) {
   const int group = num_q_heads / num_kv_heads;
   const int head_tiles = (group + 15) / 16;
-  const int seg_chunks = g_seg_chunks.load();
+  const int seg_chunks = num_groups > 0 ? 0 : g_seg_chunks.load();
   const int64_t max_chunks = chunk_bound(num_seqs, (int64_t)num_kv_heads * head_tiles,
                                          (int64_t)max_blocks_per_seq * block_size, seg_chunks);
   const int workers = decode_workers(max_chunks);
   if (!split_fits(max_chunks, workers))
     return fail(PKV_EUNSUPPORTED, "problem too large for the split arithmetic");
-  const size_t need = pkv::decode_workspace_bytes(num_seqs, num_kv_heads, group, head_dim, workers);
+  const size_t need = num_groups > 0
+                          ? pkv::decode_prefix_workspace_bytes(num_seqs, num_kv_heads, group, head_dim, workers,
+                                                               num_groups)
+                          : pkv::decode_workspace_bytes(num_seqs, num_kv_heads, group, head_dim, workers);
   if (!workspace || workspace_bytes < need)
     return fail(PKV_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
@@ -446,6 +449,7 @@ static int run_decode(float* out, const void* query, const void* key_cache, cons
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.group = group;
+  a.head_dim = head_dim;
   a.head_tiles = head_tiles;
   a.tile_cols = group < 16 ? group : 16;
   a.num_blocks = num_blocks;
@@ -461,7 +465,12 @@ static int run_decode(float* out, const void* query, const void* key_cache, cons
   a.v_inv = fmt.kind == pkv::KvKind::FP8 ? 1.0f / fmt.v_scale : 1.0f;
   a.prefill_plan = prefill_plan;
   a.prefill_max_tok = max_blocks_per_seq * block_size;
-  pkv::decode_workspace_carve(a, workspace, head_dim);
+  a.groups = groups;
+  a.num_groups = num_groups;
+  if (num_groups > 0)
+    pkv::decode_prefix_workspace_carve(a, workspace, head_dim);
+  else
+    pkv::decode_workspace_carve(a, workspace, head_dim);
   (void)max_seq_len;
   hipError_t e = pkv::launch_decode(a, head_dim, block_size, fmt.kind, stream, g_ev_start, g_ev_stop);
   return e == hipSuccess ? ok() : hip_fail(e, "decode launch");
@@ -472,10 +481,20 @@ static int decode_impl(float* out, const void* query, const void* key_cache, con
                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale, pkv_dtype dtype,
                        KvFormat fmt, void* workspace, size_t workspace_bytes, void* stream,
-                       const void* new_k = nullptr, const void* new_v = nullptr) {
+                       const void* new_k = nullptr, const void* new_v = nullptr,
+                       const int32_t* groups = nullptr, int32_t num_groups = 0) {
   int st = check_shape(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || num_seqs > kMaxSeqs) return fail(PKV_EUNSUPPORTED, "num_seqs %d (max %d)", num_seqs, kMaxSeqs);
+  if (num_groups < 0) return fail(PKV_EINVAL, "num_groups %d", num_groups);
+  if (num_groups > 0) {
+    if (dtype == PKV_F32) return fail(PKV_EUNSUPPORTED, "shared prefixes need bf16 or E4M3 pools");
+    if (num_groups > pkv::kMaxPrefixGroups)
+      return fail(PKV_EUNSUPPORTED, "num_groups %d (max %d)", num_groups, pkv::kMaxPrefixGroups);
+    if (num_seqs > pkv::kMaxPrefixSeqs)
+      return fail(PKV_EUNSUPPORTED, "num_seqs %d with shared prefixes (max %d)", num_seqs, pkv::kMaxPrefixSeqs);
+    if (!groups) return fail(PKV_EINVAL, "null pointer (prefix groups)");
+  }
   if (max_blocks_per_seq < 0 || num_blocks < 0 || max_seq_len < 0)
     return fail(PKV_EINVAL, "negative size");
   st = check_attention_bounds(max_blocks_per_seq, block_size, num_blocks, num_kv_heads, head_dim, dtype);
@@ -489,7 +508,8 @@ static int decode_impl(float* out, const void* query, const void* key_cache, con
   if (max_blocks_per_seq > 0 && num_blocks == 0) return fail(PKV_EINVAL, "empty pool with a non-empty block table");
   return run_decode(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens, nullptr,
                     num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_seq_len,
-                    scale, fmt, workspace, workspace_bytes, static_cast<hipStream_t>(stream), new_k, new_v);
+                    scale, fmt, workspace, workspace_bytes, static_cast<hipStream_t>(stream), new_k, new_v,
+                    nullptr, groups, num_groups);
 }
 
 int pkv_paged_attention_decode(float* out, const void* query, const void* key_cache,
@@ -613,6 +633,61 @@ int pkv_paged_attention_decode_noalloc(float* out, const void* query, const void
   return decode_impl(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_seq_len, scale, dtype,
                      plain_format(dtype), ws, kScratchBytes, stream);
+}
+
+size_t pkv_decode_shared_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, pkv_dtype dtype, int32_t num_groups) {
+  if (num_seqs < 0 || num_seqs > pkv::kMaxPrefixSeqs || num_groups < 0 || num_groups > pkv::kMaxPrefixGroups)
+    return 0;
+  if (dtype == PKV_F32 || check_shape(num_q_heads, num_kv_heads, head_dim, block_size, dtype) != PKV_OK) return 0;
+  return pkv::decode_prefix_workspace_bytes(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim,
+                                            decode_workers(), num_groups);
+}
+
+int pkv_paged_attention_decode_shared(float* out, const void* query, const void* key_cache,
+                                      const void* value_cache, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
+                                      pkv_dtype dtype, const int32_t* prefix_groups, int32_t num_groups,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype == PKV_FP8_E4M3)
+    return fail(PKV_EINVAL, "E4M3 pools need their scales: use pkv_paged_attention_decode_shared_fp8");
+  return decode_impl(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_seq_len, scale, dtype,
+                     plain_format(dtype), workspace, workspace_bytes, stream, nullptr, nullptr, prefix_groups,
+                     num_groups);
+}
+
+int pkv_paged_attention_decode_shared_fp8(float* out, const void* query, const void* key_cache,
+                                          const void* value_cache, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                          int64_t num_blocks, int32_t block_size, int32_t max_seq_len, float scale,
+                                          float k_scale, float v_scale, const int32_t* prefix_groups,
+                                          int32_t num_groups, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  if (!good_scale(k_scale) || !good_scale(v_scale))
+    return fail(PKV_EINVAL, "k_scale %g / v_scale %g must be positive and finite", k_scale, v_scale);
+  return decode_impl(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_seq_len, scale,
+                     PKV_FP8_E4M3, KvFormat{pkv::KvKind::FP8, k_scale, v_scale}, workspace, workspace_bytes,
+                     stream, nullptr, nullptr, prefix_groups, num_groups);
+}
+
+int pkv_decode_step_shared(float* out, const void* query, const void* key, const void* value, void* key_cache,
+                           void* value_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t max_seq_len,
+                           float scale, pkv_dtype dtype, const int32_t* prefix_groups, int32_t num_groups,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype == PKV_FP8_E4M3) return fail(PKV_EINVAL, "E4M3 pools need their scales");
+  if (num_seqs > 0 && (!key || !value)) return fail(PKV_EINVAL, "null pointer");
+  if (!aligned16(key) || !aligned16(value)) return fail(PKV_EINVAL, "key/value must be 16-byte aligned");
+  return decode_impl(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_seq_len, scale, dtype,
+                     plain_format(dtype), workspace, workspace_bytes, stream, key, value, prefix_groups,
+                     num_groups);
 }
 
 static size_t varlen_decode_part(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {

@@ -27,6 +27,7 @@ struct DecodeArgs {
   int num_q_heads;
   int num_kv_heads;
   int group;                  // Hq / Hkv
+  int head_dim;
   int head_tiles;             // ceil(group / 16)
   int tile_cols;              // min(group, 16)
   int64_t num_blocks;
@@ -58,7 +59,19 @@ struct DecodeArgs {
   // kernel's item plan here, for tables of prefill_max_tok tokens.
   int* prefill_plan;
   int prefill_max_tok;
+  // Optional shared prefixes (the *_shared calls): groups int32 [num_groups][3]
+  // = (first sequence, number of sequences, shared tokens).  The sequences of
+  // a group read their first shared tokens through the first member's block
+  // table in one pass for all their query heads.
+  const int32_t* groups;
+  int num_groups;
+  int pre_pairs_cap;          // prefix pairs the workspace holds
   // workspace
+  int* seq_group;             // [B] each sequence's group or -1 (prefix calls; split kernel writes it)
+  int* gchunk;                // [num_groups + 1] chunk prefix sums of the prefix region
+  int* gpair;                 // [num_groups + 1] prefix-pair prefix sums
+  float* pre_ml;              // [pre slots][prefix_cols][2]  prefix parts: (max, sum) per column
+  float* pre_o;               // [pre slots][prefix_cols][D]  prefix parts: unnormalised outputs
   int* cum;                   // [B + 1] chunk prefix sums (written by the split kernel)
   int* counter;               // the units taken so far (the workspace's first word)
   float* part_ml;             // [slots, tile_cols, 2]  (max, sum) in the log2 domain
@@ -68,6 +81,16 @@ struct DecodeArgs {
 size_t decode_workspace_bytes(int num_seqs, int num_kv_heads, int group, int head_dim, int workers);
 // Splits the workspace into the DecodeArgs pointers.
 void decode_workspace_carve(DecodeArgs& a, void* ws, int head_dim);
+// Shared-prefix calls: the decode workspace followed by the prefix region's
+// tables and parts (num_groups groups).
+size_t decode_prefix_workspace_bytes(int num_seqs, int num_kv_heads, int group, int head_dim, int workers,
+                                     int num_groups);
+void decode_prefix_workspace_carve(DecodeArgs& a, void* ws, int head_dim);
+// Query columns of one prefix pair: four MFMA column tiles for head_dim 64,
+// two for 128 (four would not fit the registers of a double-buffered pass).
+constexpr int prefix_cols(int head_dim) { return head_dim == 128 ? 32 : 64; }
+constexpr int kMaxPrefixGroups = 1024;
+constexpr int kMaxPrefixSeqs = 4096;
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int block_size, KvKind kind,
                          hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);

@@ -51,6 +51,16 @@ _SIGNATURES = {
     "pkv_decode_step_fp8": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32,
                                      _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_f32, _c_f32, _c_f32, _c_vp,
                                      _c_sz, _c_vp]),
+    "pkv_decode_shared_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pkv_paged_attention_decode_shared": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32, _c_i32,
+                                                   _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_f32, _c_i32, _c_vp,
+                                                   _c_i32, _c_vp, _c_sz, _c_vp]),
+    "pkv_paged_attention_decode_shared_fp8": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32,
+                                                       _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_f32, _c_f32,
+                                                       _c_f32, _c_vp, _c_i32, _c_vp, _c_sz, _c_vp]),
+    "pkv_decode_step_shared": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32,
+                                        _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_f32, _c_i32, _c_vp, _c_i32,
+                                        _c_vp, _c_sz, _c_vp]),
     "pkv_paged_attention_decode_noalloc": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32,
                                                     _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_f32, _c_i32,
                                                     _c_vp]),
@@ -253,6 +263,93 @@ def paged_attention_decode_noalloc(query: torch.Tensor, key_cache: torch.Tensor,
         _dev(value_cache, "value_cache", ndim=4), _dev(block_tables, "block_tables", torch.int32, 2),
         block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32, 1), B, Hq, Hkv, D, NB, bs,
         int(max_seq_len), float(scale), _kv_dtype(query), _stream(query)), "paged_attention_decode_noalloc")
+    return out
+
+
+def _groups(prefix_groups: torch.Tensor):
+    g = prefix_groups
+    if g.dim() != 2 or g.shape[1] != 3:
+        raise ValueError("prefix_groups must be int32 [num_groups, 3]")
+    return _dev(g, "prefix_groups", torch.int32, 2), int(g.shape[0])
+
+
+def decode_shared_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                 block_size: int, dtype, num_groups: int) -> int:
+    kind = PKV_FP8_E4M3 if dtype == torch.uint8 else (PKV_BF16 if dtype == torch.bfloat16 else PKV_F32)
+    return int(lib().pkv_decode_shared_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                                      kind, num_groups))
+
+
+def paged_attention_decode_shared(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                                  block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                                  max_seq_len: int, prefix_groups: torch.Tensor, out: Optional[torch.Tensor] = None,
+                                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """paged_attention_decode where prefix_groups (int32 [G, 3]: first sequence,
+    sequences, shared tokens) names sequences whose first tokens live in the
+    same blocks; each group's shared blocks are read once."""
+    B, Hq, D = query.shape
+    NB, bs, Hkv, Dk = key_cache.shape
+    if Dk != D or value_cache.shape != key_cache.shape or query.dtype != key_cache.dtype:
+        raise ValueError("cache shapes or dtypes disagree with the query")
+    gp, ng = _groups(prefix_groups)
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=query.device)
+    ws = _workspace(decode_shared_workspace_size(B, Hq, Hkv, D, bs, query.dtype, ng), query.device, workspace)
+    _check(lib().pkv_paged_attention_decode_shared(
+        _dev(out, "out", torch.float32, 3), _dev(query, "query", ndim=3), _dev(key_cache, "key_cache", ndim=4),
+        _dev(value_cache, "value_cache", ndim=4), _dev(block_tables, "block_tables", torch.int32, 2),
+        block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32, 1), B, Hq, Hkv, D, NB, bs,
+        int(max_seq_len), float(scale), _kv_dtype(query), gp, ng, _dev(ws, "workspace"),
+        ws.numel() * ws.element_size(), _stream(query)), "paged_attention_decode_shared")
+    return out
+
+
+def paged_attention_decode_shared_fp8(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                                      block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                                      max_seq_len: int, k_scale: float, v_scale: float, prefix_groups: torch.Tensor,
+                                      out: Optional[torch.Tensor] = None,
+                                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """paged_attention_decode_fp8 with shared-prefix groups (bf16 query, E4M3 pools)."""
+    B, Hq, D = query.shape
+    NB, bs, Hkv, Dk = key_cache.shape
+    if key_cache.dtype != torch.uint8 or query.dtype != torch.bfloat16 or Dk != D:
+        raise ValueError("E4M3 pools (uint8) and a bfloat16 query are required")
+    gp, ng = _groups(prefix_groups)
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=query.device)
+    ws = _workspace(decode_shared_workspace_size(B, Hq, Hkv, D, bs, torch.uint8, ng), query.device, workspace)
+    _check(lib().pkv_paged_attention_decode_shared_fp8(
+        _dev(out, "out", torch.float32, 3), _dev(query, "query", ndim=3), _dev(key_cache, "key_cache", ndim=4),
+        _dev(value_cache, "value_cache", ndim=4), _dev(block_tables, "block_tables", torch.int32, 2),
+        block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32, 1), B, Hq, Hkv, D, NB, bs,
+        int(max_seq_len), float(scale), float(k_scale), float(v_scale), gp, ng, _dev(ws, "workspace"),
+        ws.numel() * ws.element_size(), _stream(query)), "paged_attention_decode_shared_fp8")
+    return out
+
+
+def decode_step_shared(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                       value_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                       max_seq_len: int, prefix_groups: torch.Tensor, out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """decode_step with shared-prefix groups: each sequence's new token is
+    written to its slot, then attention reads each group's shared blocks once."""
+    B, Hq, D = query.shape
+    NB, bs, Hkv, Dk = key_cache.shape
+    if Dk != D or value_cache.shape != key_cache.shape or query.dtype != key_cache.dtype:
+        raise ValueError("cache shapes or dtypes disagree with the query")
+    if key.shape != (B, Hkv, D) or value.shape != (B, Hkv, D):
+        raise ValueError("key/value must be [num_seqs, num_kv_heads, head_dim]")
+    gp, ng = _groups(prefix_groups)
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=query.device)
+    ws = _workspace(decode_shared_workspace_size(B, Hq, Hkv, D, bs, query.dtype, ng), query.device, workspace)
+    _check(lib().pkv_decode_step_shared(
+        _dev(out, "out", torch.float32, 3), _dev(query, "query", ndim=3), _dev(key, "key", ndim=3),
+        _dev(value, "value", ndim=3), _dev(key_cache, "key_cache", ndim=4), _dev(value_cache, "value_cache", ndim=4),
+        _dev(block_tables, "block_tables", torch.int32, 2), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens", torch.int32, 1), B, Hq, Hkv, D, NB, bs, int(max_seq_len), float(scale),
+        _kv_dtype(query), gp, ng, _dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream(query)),
+        "decode_step_shared")
     return out
 
 

@@ -224,3 +224,20 @@ def test_noalloc_decode_validation_runs_before_any_launch():
     assert call(B=9000) == 2
     assert call(B=4096, Hq=64, Hkv=8) == 2
     assert b"scratch" in lib.pkv_last_error()
+
+
+def test_shared_prefix_decode_validation_runs_before_any_launch():
+    lib = ops.lib()
+
+    def call(B=2, dtype=1, groups=1 << 20, ng=1):
+        p = 1 << 20
+        return lib.pkv_paged_attention_decode_shared(p, p, p, p, p, 4, p, B, 8, 2, 128, 16, 16, 64, 0.1, dtype,
+                                                     groups, ng, p, 1 << 30, None)
+    assert call(dtype=0) == 2                          # float32 pools
+    assert call(ng=2000) == 2
+    assert call(ng=-1) == 1
+    assert call(groups=None) == 1
+    assert call(B=5000) == 2
+    assert call(dtype=2) == 1                          # E4M3 needs the _fp8 call
+    assert lib.pkv_decode_shared_workspace_size(2, 8, 2, 128, 16, 1, 1) > lib.pkv_decode_workspace_size(2, 8, 2, 128, 16, 1)
+    assert lib.pkv_decode_shared_workspace_size(2, 8, 2, 128, 16, 0, 1) == 0
