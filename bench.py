@@ -49,7 +49,7 @@ HBM_PEAK_GBPS = 8000.0
 W_BF16_NAN = np.uint16(0x7FC0)                # the workloads' free-slot poison (bf16 NaN)
 MFMA_BF16_TFLOPS = 2500.0
 METRIC = "paged-attn decode KV GB/s (% of MI355X HBM peak); seq-tokens/s per step"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_97_amd/csrc/decode_kernels.hip", "paged_kv_cache_97_amd/csrc/common.h",
                   "paged_kv_cache_97_amd/csrc/tiles.h", "paged_kv_cache_97_amd/csrc/launch.h"]
 CALIB_BYTES = 256 << 20
@@ -65,15 +65,19 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _load_traffic():
-    """Counter-measured HBM bytes per launch of the split kernel, if they were
-    taken on the current kernel source; else None."""
+def traffic_key(cfg: int, fp8: bool) -> str:
+    return "config%d-%s" % (cfg, "fp8" if fp8 else "auto")
+
+
+def _load_traffic(key: str):
+    """Counter-measured HBM bytes per launch of a workload's split kernel, if
+    they were taken on the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            rec = json.load(f).get(key)
+    except (OSError, ValueError, AttributeError):
         return None
-    if rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != kernel_source_hash():
         return None
     return rec
 
@@ -107,7 +111,7 @@ def summarize(fetch_dir: str, write_dir: str, kv_bytes: int, cmd: str) -> dict:
                         "kernels": {k: {"dispatches": len(v), "raw_kib_mean": sum(v) / len(v),
                                         "bytes_per_launch": sum(v) / len(v) * 1024.0 * factor}
                                     for k, v in per.items()}}
-    split = [k for k in out["FETCH_SIZE"]["kernels"] if "decode_split_kernel" in k]
+    split = [k for k in out["FETCH_SIZE"]["kernels"] if "decode_split" in k]
     rec = {"source_hash": kernel_source_hash(), "command": cmd, "algorithmic_kv_bytes": kv_bytes,
            "counters": out}
     if split:
@@ -596,7 +600,7 @@ def _roofline(case: GpuCase, kern_ms: list) -> dict:
                 "kernel_ms_min": round(float(np.min(kern_ms)), 5), "flops_per_launch": flops}
     kvb = case.kv_bytes()
     achieved = kvb / (k_mean * 1e-3) / 1e9
-    tr = _load_traffic() if case.cfg == 3 and not case.fp8 else None
+    tr = None if case.varlen else _load_traffic(traffic_key(case.cfg, case.fp8))
     return {"bound": "hbm", "kernel": case.kernel_name(), "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": round(tr["traffic_bytes_per_launch"]) if tr else None,
@@ -693,11 +697,19 @@ def main() -> int:
     args = ap.parse_args()
     if args.summarize:
         from paged_kv_cache_97_amd import workloads as W
-        wl = W.generate(args.config or 3)
-        rec = summarize(args.summarize[0], args.summarize[1], wl.kv_bytes_logical(), args.command)
+        cfg = args.config or 3
+        fp8 = args.kv_cache_dtype == "fp8"
+        wl = W.generate(cfg)
+        rec = summarize(args.summarize[0], args.summarize[1], wl.kv_bytes_logical() // (2 if fp8 else 1), args.command)
         os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        try:
+            with open(TRAFFIC_FILE) as f:
+                allrec = json.load(f)
+        except (OSError, ValueError):
+            allrec = {}
+        allrec[traffic_key(cfg, fp8)] = rec
         with open(TRAFFIC_FILE, "w") as f:
-            json.dump(rec, f, indent=1)
+            json.dump(allrec, f, indent=1)
         print(json.dumps({k: v for k, v in rec.items() if k != "counters"}))
         return 0
     if args.gpus != 1:

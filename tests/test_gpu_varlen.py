@@ -76,6 +76,17 @@ def test_any_finite_scale(name, scale, dev):
     _check(wl, dev, "%s scale %g" % (name, scale), max(1.0, abs(scale) * np.sqrt(wl.spec.head_dim)))
 
 
+@pytest.mark.parametrize("scale", [3.0, 8.0])
+@pytest.mark.parametrize("name", ["gqa8-bs16", "gqa8-long-chunk", "gqa4-bs32"])
+def test_scores_far_beyond_the_first_chunk(name, scale, dev):
+    """Scales so large that later keys' scores exceed a column's early
+    maxima by far more than the prefill kernel's rescale slack, many times
+    per column: the running references must move exactly."""
+    wl = W.generate(SMALL[name], seed=32)
+    wl.scale = float(scale)
+    _check(wl, dev, "%s scale %g" % (name, scale), max(1.0, abs(scale) * np.sqrt(wl.spec.head_dim)))
+
+
 def test_more_prefill_sequences_than_the_plan_sorts(dev):
     """600 prefill chunks in one step: past the 512 the plan orders by
     length, the work items follow the batch order instead."""
