@@ -365,7 +365,16 @@ size_t pkv_varlen_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
  *   num_tokens; max_query_len >= every q_s (host scalar); seq_lens[s] >= q_s.
  *   Rows of a sequence with seq_lens[s] < q_s are unspecified.
  *   workspace >= pkv_varlen_workspace_size(...) bytes, 256-byte aligned.
+ *                Its first 8 bytes hold work counters: they must be zero
+ *                before the first call that uses it (zero-fill a new
+ *                workspace once); every call leaves them zero.  Calls
+ *                sharing a workspace must not overlap.
  *   num_seqs <= 8192.
+ *   The decode rows run first, through the split and merge kernels, then
+ *   the chunks.  After pkv_set_varlen_single_launch(1), calls with bfloat16
+ *   or E4M3 pools, head_dim 128, max_query_len > 1 and num_seqs <= 2048 run
+ *   both in one launch instead (the decode rows' work queued after the
+ *   chunks').
  */
 int pkv_paged_attention_varlen(float* out, const void* query, const void* key_cache,
                                const void* value_cache, const int32_t* block_tables,
@@ -457,6 +466,12 @@ int pkv_swap_blocks(const void* src_key, const void* src_value, void* dst_key, v
  * do not depend on it beyond float reordering.  Returns the previous value
  * (-1 for an out-of-range argument).
  *
+ * pkv_set_varlen_single_launch: 1 runs the mixed varlen calls described at
+ * pkv_paged_attention_varlen in one launch, 0 (default) in the split +
+ * merge + prefill launches (same results up to float reordering; the one
+ * launch is the slower of the two on MI355X).  Returns the previous value
+ * (-1 for an argument other than 0 or 1).
+ *
  * pkv_set_decode_dynamic: the share (permille, 0..500) of the decode
  * split's chunks that is handed out in units of at least unit_chunks chunks
  * (1..4096, default 4) from a counter, to the wavefronts that finish their
@@ -486,6 +501,7 @@ int pkv_set_decode_workers(int32_t workers);
 int pkv_set_waves_per_cu(int32_t waves);
 int pkv_set_decode_segment_cost(int32_t chunks);
 int pkv_set_decode_dynamic(int32_t permille, int32_t unit_chunks);
+int pkv_set_varlen_single_launch(int32_t on);
 int pkv_get_waves_per_cu(void);
 
 #ifdef __cplusplus

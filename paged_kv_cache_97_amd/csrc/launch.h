@@ -153,6 +153,16 @@ hipError_t launch_prefill_lds(const PrefillArgs& a, int block_size, bool fp8, in
 // (PrefillArgs::plan) must have been built beforehand (DecodeArgs::prefill_plan).
 bool prefill_uses_plan(int head_dim, KvKind kind);
 
+// Mixed varlen steps whose prefill rows use the workgroup-shared kernel:
+// prefill and decode rows in one launch of `grid` workgroups (one per
+// compute unit).  The workspace holds the item counter and the count of
+// finished workgroups (words 0 and 1, zero on entry and left zero) and
+// 8 part slots per workgroup for the decode rows.  num_seqs <= kMixedMaxSeqs.
+constexpr int kMixedMaxSeqs = 2048;
+size_t mixed_workspace_bytes(int grid, int tile_cols, int head_dim);
+hipError_t launch_mixed_varlen(const PrefillArgs& p, DecodeArgs d, void* workspace, int block_size, bool fp8,
+                               int grid, hipStream_t stream);
+
 // Whole-block copies for every (src, dst) pair of mapping (int64 [pairs][2]);
 // src1/dst1 may be null (one pool).  Pairs with an id outside its pool are
 // skipped.  streaming: non-temporal loads and stores (copies inside device

@@ -83,6 +83,7 @@ _SIGNATURES = {
     "pkv_set_waves_per_cu": (_c_i32, [_c_i32]),
     "pkv_set_decode_segment_cost": (_c_i32, [_c_i32]),
     "pkv_set_decode_dynamic": (_c_i32, [_c_i32, _c_i32]),
+    "pkv_set_varlen_single_launch": (_c_i32, [_c_i32]),
     "pkv_get_waves_per_cu": (_c_i32, []),
 }
 
@@ -624,6 +625,22 @@ def set_decode_dynamic(permille: int, unit_chunks: int = 4) -> int:
     unit_chunks chunks to the wavefronts that finish first (-1: chosen per
     call); returns the previous share."""
     return int(lib().pkv_set_decode_dynamic(int(permille), int(unit_chunks)))
+
+
+def varlen_single_launch() -> bool:
+    """The current setting of set_varlen_single_launch."""
+    prev = set_varlen_single_launch(True)
+    set_varlen_single_launch(prev)
+    return prev
+
+
+def set_varlen_single_launch(on: bool) -> bool:
+    """Whether mixed varlen steps (bf16/E4M3 pools, head_dim 128) run prefill
+    and decode rows in one launch; returns the previous setting."""
+    r = int(lib().pkv_set_varlen_single_launch(1 if on else 0))
+    if r < 0:
+        raise PagedKVError("pkv_set_varlen_single_launch failed")
+    return bool(r)
 
 
 def set_waves_per_cu(n: int) -> int:

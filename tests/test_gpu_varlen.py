@@ -105,10 +105,91 @@ def test_mixed_batch_of_the_page_example(dev, golden):
     _check(wl, dev, "page-example")
 
 
+class launches:
+    """Mixed varlen calls in one launch (single=True) or through the split +
+    merge + prefill launches (the default)."""
+    def __init__(self, single: bool):
+        self.single = single
+
+    def __enter__(self):
+        self.prev = ops.set_varlen_single_launch(self.single)
+
+    def __exit__(self, *exc):
+        ops.set_varlen_single_launch(self.prev)
+
+
+# shapes whose prefill chunks take the workgroup-shared kernel (bf16, head_dim 128)
+ONE_LAUNCH = ["decode-first", "gqa32", "gqa4-bs32", "gqa6-odd", "gqa8-bs16", "gqa8-long-chunk",
+              "gqa8-pure-prefill", "mha-d128"]
+
+
+@pytest.mark.parametrize("name", ONE_LAUNCH)
+def test_reduced_shapes_one_launch(name, dev):
+    """The same steps with prefill chunks and decode rows in one launch."""
+    with launches(single=True):
+        _check(W.generate(SMALL[name], seed=103), dev, name + " (1 launch)")
+
+
+def test_config5_full_size_one_launch(dev):
+    with launches(single=True):
+        _check(W.generate(5), dev, "config 5 (1 launch)")
+
+
+# decode rows of 1 .. 4,001 tokens (each listed context + the new token): one chunk, a ragged last chunk, ranges on 2 .. 8 waves
+DECODE_LENS = (0, 1, 5, 10, 15, 16, 17, 31, 32, 33, 50, 63, 64, 65, 96, 100, 128, 200, 255, 256, 257, 300,
+               511, 512, 513, 700, 1000, 1023, 1024, 1025, 1500, 2000, 2047, 2048, 2049, 2500, 3000, 3500,
+               3999, 4000)
+
+
+def _decode_heavy(**kw):
+    return _mixed(num_decode=len(DECODE_LENS), num_prefill=2, prefill_chunk=20, prefill_ctx=("uniform", 0, 100),
+                  decode_len=("fixed", DECODE_LENS), **kw)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(block_size=32), dict(num_q_heads=64, num_kv_heads=2),
+                                dict(num_q_heads=40, num_kv_heads=8)], ids=["gqa8", "bs32", "gqa32", "gqa5"])
+def test_one_launch_decode_rows(kw, dev):
+    """Many decode rows of very different lengths (1 to 4,000 tokens: rows
+    of one chunk, and rows split over all 8 waves of a workgroup) queued
+    behind two small prefill chunks, with one and with several head tiles,
+    in one launch and in three."""
+    for single in (True, False):
+        with launches(single):
+            _check(W.generate(_decode_heavy(**kw), seed=44), dev, "decode-heavy %s single=%d" % (kw, single))
+
+
+def test_one_launch_is_deterministic_and_leaves_its_counters_zero(dev):
+    """Which workgroup runs an item varies from run to run, the results do
+    not (every item's split is fixed by its row); the last workgroup resets
+    the workspace's counters for the next call."""
+    wl = W.generate(_decode_heavy(), seed=45)
+    t = upload(wl, dev)
+    run_step(wl, t, decode=False)                      # writes the step's K/V
+    B, T = wl.num_seqs, wl.num_tokens
+    Hq, Hkv, D = wl.spec.num_q_heads, wl.spec.num_kv_heads, wl.spec.head_dim
+    nbytes = ops.varlen_workspace_size(B, T, Hq, Hkv, D, wl.max_query_len, wl.spec.block_size, t["query"].dtype)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    outs = []
+    with launches(single=True):
+        for _ in range(3):
+            outs.append(ops.paged_attention_varlen(t["query"], t["key_cache"], t["value_cache"], t["block_tables"],
+                                                   t["seq_lens"], t["query_start_loc"], wl.scale, wl.max_query_len,
+                                                   wl.max_seq_len, workspace=ws))
+            torch.cuda.synchronize()
+            assert int(ws[:8].view(torch.int32).abs().sum()) == 0, "counters not reset"
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    assert torch.equal(outs[0].view(torch.int32), outs[2].view(torch.int32))
+    r_out = oracle_step(wl, decode=False)[3]
+    assert_attn_close(outs[0], r_out, wl.spec.dtype, "deterministic")
+
+
 def test_decode_rows_equal_decode_call_bitwise(dev):
+    """With the decode rows in their own launches, they run the decode
+    call's kernels on the same split: bit-identical rows."""
     wl = W.generate(SMALL["gqa8-bs16"], seed=21)
     t = upload(wl, dev)
-    _, out = run_step(wl, t, decode=False)
+    with launches(single=False):
+        _, out = run_step(wl, t, decode=False)
     dec = np.where(~wl.is_prefill)[0]
     rows = torch.from_numpy(wl.query_start_loc[dec].astype(np.int64)).to(dev)
     idx = torch.from_numpy(dec.astype(np.int64)).to(dev)
