@@ -50,7 +50,8 @@ W_BF16_NAN = np.uint16(0x7FC0)                # the workloads' free-slot poison 
 MFMA_BF16_TFLOPS = 2500.0
 METRIC = "paged-attn decode KV GB/s (% of MI355X HBM peak); seq-tokens/s per step"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNEL_SOURCES = ["paged_kv_cache_97_amd/csrc/decode_kernels.hip", "paged_kv_cache_97_amd/csrc/common.h",
+KERNEL_SOURCES = ["paged_kv_cache_97_amd/csrc/decode_kernels.hip", "paged_kv_cache_97_amd/csrc/decode_segment.h",
+                  "paged_kv_cache_97_amd/csrc/common.h",
                   "paged_kv_cache_97_amd/csrc/tiles.h", "paged_kv_cache_97_amd/csrc/launch.h"]
 CALIB_BYTES = 256 << 20
 FP8_K_SCALE, FP8_V_SCALE = 0.0125, 0.02      # per-pool scales of the E4M3 runs
