@@ -476,7 +476,7 @@ int pkv_swap_blocks(const void* src_key, const void* src_value, void* dst_key, v
  * split's chunks that is handed out in units of at least unit_chunks chunks
  * (1..4096, default 4) from a counter, to the wavefronts that finish their
  * static range first (the rest is split in equal static ranges).  0 gives a
- * fully static split; -1 (the default) chooses per call: 100 for E4M3
+ * fully static split; -1 (the default) chooses per call: 200 for E4M3
  * pools, 120 when the call has at most one (sequence, KV head, head tile)
  * pair per four workers, else 0.  Every unit's range is fixed by the call's
  * arguments, so results do not depend on which wavefront ran it.  Returns

@@ -135,8 +135,8 @@ int64_t chunk_bound(int64_t num_seqs, int64_t pairs_per_seq, int64_t max_tokens,
 bool split_fits(int64_t chunks, int64_t workers) { return chunks < (int64_t(1) << 40) && workers <= 65536; }
 
 // Share (permille) of a decode split's chunks handed out as units to the
-// wavefronts that finish first.  Measured on MI355X: E4M3 pools gain 8 % from
-// 80-120 (their static split ends with a long tail of late waves), so do
+// wavefronts that finish first.  Measured on MI355X: E4M3 pools gain 7 % from
+// 150-200 (their static split ends with a long tail of late waves), so do
 // batches of few long (sequence, KV head) pairs -- at most one pair per four
 // workers, each pair spread over many workers -- (6 % on 16 sequences of
 // 16k-32k tokens); batches of many short pairs lose 1-2 %, so they keep a
@@ -144,7 +144,7 @@ bool split_fits(int64_t chunks, int64_t workers) { return chunks < (int64_t(1) <
 int dynamic_share(pkv::KvKind kind, int64_t pairs, int workers) {
   const int forced = g_dyn_permille.load();
   if (forced >= 0) return forced;
-  if (kind == pkv::KvKind::FP8) return 100;
+  if (kind == pkv::KvKind::FP8) return 200;
   return 4 * pairs <= workers ? 120 : 0;
 }
 
