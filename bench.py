@@ -50,9 +50,13 @@ W_BF16_NAN = np.uint16(0x7FC0)                # the workloads' free-slot poison 
 MFMA_BF16_TFLOPS = 2500.0
 METRIC = "paged-attn decode KV GB/s (% of MI355X HBM peak); seq-tokens/s per step"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+# The decode kernels and the host code that sets their split (worker count,
+# segment cost, dynamic share): a stored counter record is used only while
+# all of these are unchanged.
 KERNEL_SOURCES = ["paged_kv_cache_97_amd/csrc/decode_kernels.hip", "paged_kv_cache_97_amd/csrc/decode_segment.h",
                   "paged_kv_cache_97_amd/csrc/common.h",
-                  "paged_kv_cache_97_amd/csrc/tiles.h", "paged_kv_cache_97_amd/csrc/launch.h"]
+                  "paged_kv_cache_97_amd/csrc/tiles.h", "paged_kv_cache_97_amd/csrc/launch.h",
+                  "paged_kv_cache_97_amd/csrc/api.hip"]
 CALIB_BYTES = 256 << 20
 FP8_K_SCALE, FP8_V_SCALE = 0.0125, 0.02      # per-pool scales of the E4M3 runs
 

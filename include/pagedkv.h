@@ -458,13 +458,14 @@ int pkv_swap_blocks(const void* src_key, const void* src_value, void* dst_key, v
  * pkv_set_waves_per_cu: default worker density per compute unit (4..16,
  * multiple of 4; default 4).  Returns the previous value.
  *
- * pkv_set_decode_segment_cost: virtual chunks (0..64, default 0) the decode
+ * pkv_set_decode_segment_cost: virtual chunks (0..64, default 2) the decode
  * split charges for each (sequence, KV head) range a worker starts, so that
  * workers crossing more ranges get fewer real chunks (a new range costs a
- * dependent block-table load and a first-chunk round trip, about three
- * chunks of streaming on MI355X).  0 splits by real chunks only.  Results
- * do not depend on it beyond float reordering.  Returns the previous value
- * (-1 for an out-of-range argument).
+ * dependent block-table load and a first-chunk round trip, two to three
+ * chunks of streaming on MI355X).  0 splits by real chunks only.  The
+ * shared-prefix calls always split by real chunks.  Results do not depend
+ * on it beyond float reordering.  Returns the previous value (-1 for an
+ * out-of-range argument).
  *
  * pkv_set_varlen_single_launch: 1 runs the mixed varlen calls described at
  * pkv_paged_attention_varlen in one launch, 0 (default) in the split +

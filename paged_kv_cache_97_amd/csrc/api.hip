@@ -19,7 +19,7 @@ thread_local hipEvent_t g_ev_start = nullptr;
 thread_local hipEvent_t g_ev_stop = nullptr;
 std::atomic<int> g_workers_override{0};
 std::atomic<int> g_waves_per_cu{4};
-std::atomic<int> g_seg_chunks{0};
+std::atomic<int> g_seg_chunks{2};              // virtual chunks charged per pair started
 std::atomic<int> g_dyn_permille{-1};             // -1: chosen per call (dynamic_share)
 std::atomic<int> g_unit_chunks{4};
 std::atomic<int> g_varlen_single{0};           // mixed varlen steps in one launch (opt-in)
