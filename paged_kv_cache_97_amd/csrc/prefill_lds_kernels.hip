@@ -96,6 +96,19 @@ constexpr int kRowV = 288;                         // LDS bytes of one V token r
 typedef uint8_t KBuf[32 * kRowK];                  // one 32-token K chunk
 typedef uint8_t VBuf[32 * kRowV];                  // one 32-token V chunk
 
+// A wave-uniform address as an opaque scalar value: a load from it plus a
+// 32-bit lane offset then keeps a scalar base, instead of being re-associated
+// into per-lane 64-bit address arithmetic around a hoisted lane term.
+typedef __attribute__((address_space(1))) const char gchar;
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+__device__ __forceinline__ gchar* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<gchar*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ u32x4 gld16(gchar* p) { return *reinterpret_cast<gu32x4*>(p); }
+
 // One item: the kPfCols (row, head) columns block `local` of prefill
 // sequence s (KV head local / blocks-per-head), computed by the workgroup's 8
 // waves through the LDS chunk buffers kbuf[2] and vbuf[3].
@@ -169,21 +182,24 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int lo
   // masked scores.
   u32x4 S[2][2];
   const bool kthr = wave < kPfWaves / 2;             // FP8 only: this wave loads K
+  // A wave's loader rows lie in one of a chunk's two 16-token blocks (bf16:
+  // rows 16-31 are waves 4-7; FP8: the waves with (wave & 3) >= 2), so the
+  // block base is wave-uniform and each lane adds a constant 32-bit offset:
+  // the address arithmetic per chunk is scalar (3 % faster on the 8 x 512-row
+  // step than per-lane 64-bit addresses).
+  const bool second = BS == 16 && (FP8 ? (wave & 3) >= 2 : wave >= 4);
+  const int my_row = FP8 ? ((tid >> 3) & 31) : ld_row;
+  const uint32_t lane_off = (uint32_t)(((((BS == 16 ? (my_row & 15) : my_row) * Hkv + h) * D) +
+                                        (FP8 ? 16 * (tid & 7) : 8 * ld_chunk)) * (int)sizeof(Elem));
+  const int64_t blk_bytes = (int64_t)BS * Hkv * D * (int64_t)sizeof(Elem);
+  const char* kpool = reinterpret_cast<const char*>(FP8 && !kthr ? vc : kc);
+  const char* vpool = reinterpret_cast<const char*>(vc);
   auto load_chunk = [&](int ch, u32x4* R) {
     const int lb0 = (ch * 32) / BS;                          // uniform
-    const int b0 = win.get(lb0);
-    const int b1 = BS == 16 ? win.get(lb0 + 1) : b0;
-    auto addr = [&](const Elem* pool, int r, int elem_off) {
-      const int blk = BS == 16 && r >= 16 ? b1 : b0;
-      const int off = BS == 16 ? (r & 15) : r;
-      return pool + ((int64_t)blk * BS + off) * Hkv * D + h * D + elem_off;
-    };
-    if constexpr (FP8) {
-      R[0] = ld16(addr(kthr ? kc : vc, (tid >> 3) & 31, 16 * (tid & 7)));
-    } else {
-      R[0] = ld16(addr(kc, ld_row, 8 * ld_chunk));
-      R[1] = ld16(addr(vc, ld_row, 8 * ld_chunk));
-    }
+    const int blk = uniform(second ? win.get(lb0 + 1) : win.get(lb0));
+    const int64_t boff = (int64_t)blk * blk_bytes;
+    R[0] = gld16(uniform_ptr(kpool + boff) + lane_off);
+    if constexpr (!FP8) R[1] = gld16(uniform_ptr(vpool + boff) + lane_off);
   };
   auto store_chunk = [&](int ch, int kb, int vb, const u32x4* R) {
     if constexpr (FP8) {
