@@ -24,7 +24,11 @@
  *             stream).  Calls only enqueue kernels, in stream order, and never
  *             synchronise: one or two per call, three for a varlen call
  *             with prefill-chunk rows (decode split, merge -- which also
- *             builds the prefill kernel's item plan -- then prefill).
+ *             builds the prefill kernel's item plan -- then prefill).  The
+ *             decode rows' split-K parts need their merge after the split
+ *             kernel ends, and the prefill rows run in a persistent kernel of
+ *             their own; the one-launch form (pkv_set_varlen_single_launch)
+ *             is correct but slower on MI355X.
  *   Errors.   Arguments are validated on the host before anything is
  *             enqueued: a call that returns non-zero has enqueued nothing,
  *             except PKV_EHIP (the launch itself failed).  pkv_last_error()
