@@ -448,9 +448,43 @@ prefill_lds_kernel(const PrefillArgs a) {
   const int* order = plan + kPlanHeader;
   const int* cum = order + B;
   int* counter = a.plan + 2;
+  // XCD queues.  Workgroups are dispatched to the 8 XCDs in turn, so
+  // workgroup b runs on XCD b % 8, and each XCD has an L2 of its own.  With
+  // a KV head count that is a multiple of 8, queue x holds the items of the
+  // heads h = x (mod 8) -- per sequence in the plan's order, head by head --
+  // so one (sequence, head)'s K/V is streamed through one L2, by the
+  // workgroups of that XCD at about the same time.  A workgroup drains its
+  // own queue, then takes items from the others in turn (8 equal queues, so
+  // only the last items move).  Other head counts take items from the one
+  // counter in plan order.
+  const int Hkv = a.num_kv_heads;
+  const bool xcd_queues = Hkv % kPlanXcdQueues == 0;
+  const int x = blockIdx.x % kPlanXcdQueues, per_queue = total / kPlanXcdQueues;
+  int drained = 0;                                     // thread 0: queues found empty
   while (true) {
     __syncthreads();                                   // everyone has read the previous item
-    if (threadIdx.x == 0) s_item = atomicAdd(counter, 1);
+    if (threadIdx.x == 0) {
+      int it = total;
+      if (!xcd_queues) {
+        it = atomicAdd(counter, 1);
+      } else {
+        for (; drained < kPlanXcdQueues; ++drained) {
+          const int y = (x + drained) % kPlanXcdQueues;
+          const int j = atomicAdd(a.plan + 8 + y, 1);
+          if (j < per_queue) {
+            // Queue position j -> plan item: every sequence contributes
+            // items / 8 to each queue (its item count is Hkv x column
+            // blocks), so the sequence is the last r with cum[r] <= 8 j.
+            const int r = item_row(cum, P, kPlanXcdQueues * j);
+            const int c0 = cum[r], per_head = (cum[r + 1] - c0) / Hkv;
+            const int lj = j - c0 / kPlanXcdQueues, hi = lj / per_head;
+            it = c0 + (y + kPlanXcdQueues * hi) * per_head + (lj - hi * per_head);
+            break;
+          }
+        }
+      }
+      s_item = it;
+    }
     __syncthreads();
     const int item = s_item;
     if (item >= total) break;

@@ -10,7 +10,9 @@
 namespace pkv {
 
 constexpr int kPlanItemCols = 256;                 // (row, head) columns per prefill item
-constexpr int kPlanHeader = 16;                    // ints: [0] items, [1] prefill seqs, [2] counter
+constexpr int kPlanHeader = 16;                    // ints: [0] items, [1] prefill seqs, [2] counter,
+                                                   // [8 + x] the counter of XCD x's queue
+constexpr int kPlanXcdQueues = 8;
 constexpr int kSortMax = 512;                      // prefill sequences the plan sorts by length
 
 // Exclusive scan of f(i), i in [0, n), writing out(i, prefix) for i in [0, n]
@@ -81,6 +83,7 @@ __device__ inline void build_prefill_plan(const int32_t* __restrict__ qsl, const
     plan[0] = total;
     plan[1] = P;
     plan[2] = 0;                                       // work counter
+    for (int x = 0; x < kPlanXcdQueues; ++x) plan[8 + x] = 0;
   }
 }
 

@@ -52,6 +52,8 @@ SMALL = {
     "gqa2-d64-bs32": _mixed(num_q_heads=8, num_kv_heads=4, head_dim=64, block_size=32, prefill_chunk=64),
     "gqa6-odd": _mixed(num_q_heads=12, num_kv_heads=2, prefill_chunk=11),
     "gqa32": _mixed(num_q_heads=64, num_kv_heads=2, prefill_chunk=9),
+    # 16 KV heads: two heads in each of the prefill kernel's 8 XCD queues
+    "gqa2-kv16": _mixed(num_q_heads=32, num_kv_heads=16, prefill_chunk=45),
     "decode-first": _mixed(prefill_first=False),
     "f32-d64": _mixed(dtype="f32", num_q_heads=4, num_kv_heads=4, head_dim=64, prefill_chunk=40),
     "f32-gqa4-d128": _mixed(dtype="f32", num_q_heads=16, num_kv_heads=4, prefill_chunk=29),
