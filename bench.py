@@ -57,14 +57,20 @@ KERNEL_SOURCES = ["paged_kv_cache_97_amd/csrc/decode_kernels.hip", "paged_kv_cac
                   "paged_kv_cache_97_amd/csrc/common.h",
                   "paged_kv_cache_97_amd/csrc/tiles.h", "paged_kv_cache_97_amd/csrc/launch.h",
                   "paged_kv_cache_97_amd/csrc/api.hip"]
+# The same for the prefill kernel's record (the prefill kernel, its item
+# plan, the shared tiles and the host code that launches it).
+PREFILL_SOURCES = ["paged_kv_cache_97_amd/csrc/prefill_lds_kernels.hip", "paged_kv_cache_97_amd/csrc/prefill_plan.h",
+                   "paged_kv_cache_97_amd/csrc/common.h", "paged_kv_cache_97_amd/csrc/tiles.h",
+                   "paged_kv_cache_97_amd/csrc/launch.h", "paged_kv_cache_97_amd/csrc/varlen_kernels.hip",
+                   "paged_kv_cache_97_amd/csrc/api.hip"]
 CALIB_BYTES = 256 << 20
 FP8_K_SCALE, FP8_V_SCALE = 0.0125, 0.02      # per-pool scales of the E4M3 runs
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -74,17 +80,23 @@ def traffic_key(cfg: int, fp8: bool) -> str:
     return "config%d-%s" % (cfg, "fp8" if fp8 else "auto")
 
 
-def _load_traffic(key: str):
-    """Counter-measured HBM bytes per launch of a workload's split kernel, if
-    they were taken on the current kernel sources; else None."""
+def _load_traffic(key: str, prefill: bool = False):
+    """Counter-measured HBM bytes per launch of a workload's split kernel (or,
+    with prefill, of its prefill kernel), if they were taken on the current
+    sources of that kernel; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(key)
     except (OSError, ValueError, AttributeError):
         return None
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec:
         return None
-    return rec
+    if prefill:
+        ok = "prefill_traffic_bytes_per_launch" in rec and \
+            rec.get("prefill_source_hash") == kernel_source_hash(PREFILL_SOURCES)
+    else:
+        ok = rec.get("source_hash") == kernel_source_hash()
+    return rec if ok else None
 
 
 def summarize(fetch_dir: str, write_dir: str, kv_bytes: int, cmd: str) -> dict:
@@ -126,6 +138,13 @@ def summarize(fetch_dir: str, write_dir: str, kv_bytes: int, cmd: str) -> dict:
         rec["traffic_bytes_per_launch"] = fb + wb
         rec["fetch_bytes_per_launch"] = fb
         rec["write_bytes_per_launch"] = wb
+    pre = [k for k in out["FETCH_SIZE"]["kernels"] if "prefill_lds_kernel" in k]
+    if pre:
+        fb = out["FETCH_SIZE"]["kernels"][pre[0]]["bytes_per_launch"]
+        wb = out["WRITE_SIZE"]["kernels"].get(pre[0], {}).get("bytes_per_launch", 0.0)
+        rec.update({"prefill_kernel": pre[0], "prefill_source_hash": kernel_source_hash(PREFILL_SOURCES),
+                    "prefill_traffic_bytes_per_launch": fb + wb, "prefill_fetch_bytes_per_launch": fb,
+                    "prefill_write_bytes_per_launch": wb})
     return rec
 
 
@@ -607,9 +626,12 @@ def _roofline(case: GpuCase, kern_ms: list) -> dict:
     if case.varlen:
         flops = prefill_flops(case.wl)
         achieved = flops / (k_mean * 1e-3) / 1e12
+        tr = _load_traffic(traffic_key(case.cfg, case.fp8), prefill=True) \
+            if case.kernel_name() == "prefill_kernel" else None
         rec = {"bound": "mfma", "kernel": case.kernel_name(), "achieved": round(achieved, 2),
                "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_TFLOPS, 4),
-               "traffic": None, "kernel_ms_mean": round(k_mean, 5),
+               "traffic": round(tr["prefill_traffic_bytes_per_launch"]) if tr else None,
+               "kernel_ms_mean": round(k_mean, 5),
                "kernel_ms_min": round(float(np.min(kern_ms)), 5), "flops_per_launch": flops}
         if case.kernel_name() == "mixed_varlen_kernel":
             # the one launch also runs the decode rows: achieved charges their
