@@ -49,6 +49,34 @@ def _cases():
 
 CASES = _cases()
 
+# Varlen steps whose KV head count is a multiple of 8: the workgroup-shared
+# prefill kernel then takes its items from 8 per-XCD queues (heads h = x mod
+# 8 in queue x), with one to four heads per queue.
+WIDE_SEED = 2028
+N_WIDE = 8
+
+
+def _wide_cases():
+    rng = np.random.default_rng(WIDE_SEED)
+    out = []
+    for i in range(N_WIDE):
+        hkv = int(rng.choice([8, 16, 24, 32]))
+        g = int(rng.choice([1, 2, 3, 4]))
+        bs = int(rng.choice([16, 32]))
+        pools = str(rng.choice(["bf16", "bf16", "fp8"]))
+        spec = W.reduced(5, dtype="bf16", num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=128, block_size=bs,
+                         pool_blocks=None, num_decode=int(rng.integers(0, 5)),
+                         num_prefill=int(rng.integers(1, 6)), prefill_chunk=int(rng.integers(2, 300)),
+                         prefill_ctx=("uniform", 0, int(rng.integers(0, 600))),
+                         decode_len=("uniform", 0, int(rng.integers(1, 400))),
+                         prefill_first=bool(rng.integers(0, 2)))
+        name = "wide%02d-varlen-%s-g%d-kv%d-bs%d" % (i, pools, g, hkv, bs)
+        out.append((name, spec, pools, True, 700 + i))
+    return out
+
+
+CASES += _wide_cases()
+
 
 @pytest.fixture(scope="module")
 def dev():
