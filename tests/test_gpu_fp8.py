@@ -163,6 +163,68 @@ def test_varlen_mixed_step_fp8(dev):
         _check(W.generate(spec, seed=seed), dev, "varlen", decode=False)
 
 
+def test_config5_full_size_fp8_sampled(dev):
+    """The mixed 8 x 512-row step at full size with E4M3 pools, in the launch
+    configuration the benchmark times: the pools are quantised on the GPU by
+    the library's write (every slot), the step writes its 4,216 new tokens
+    and runs the varlen call.  The oracle quantises the blocks of a few
+    sequences itself (three prefill chunks, two decode rows) and attends over
+    them; those rows must match."""
+    wl = W.generate(5)
+    sp = wl.spec
+    qlen = np.diff(wl.query_start_loc)
+    pre = [int(s) for s in np.flatnonzero(qlen > 1)]
+    dec = [int(s) for s in np.flatnonzero(qlen == 1)]
+    by_len = sorted(pre, key=lambda s: int(wl.seq_lens[s]))
+    pre_pick = by_len[:2] + by_len[-1:]                                      # the two shortest and the longest
+    dec_pick = sorted(dec, key=lambda s: int(wl.seq_lens[s]))[len(dec) // 4:len(dec) // 4 + 2]
+    log("[fp8 config 5] B=%d T=%d NB=%d; sampled sequences %s (lengths %s)" % (
+        wl.num_seqs, wl.num_tokens, wl.num_blocks, pre_pick + dec_pick,
+        [int(wl.seq_lens[s]) for s in pre_pick + dec_pick]))
+    kc16, vc16 = to_dev(wl.key_cache, "bf16", dev), to_dev(wl.value_cache, "bf16", dev)
+    nb_slots = kc16.shape[0] * kc16.shape[1]
+    kc8 = torch.empty(kc16.shape, dtype=torch.uint8, device=dev)
+    vc8 = torch.empty(vc16.shape, dtype=torch.uint8, device=dev)
+    ops.reshape_and_cache_fp8(kc16.view(nb_slots, sp.num_kv_heads, sp.head_dim),
+                              vc16.view(nb_slots, sp.num_kv_heads, sp.head_dim), kc8, vc8,
+                              torch.arange(nb_slots, dtype=torch.int64, device=dev), K_SCALE, V_SCALE)
+    torch.cuda.synchronize()
+    del kc16, vc16
+    t = dict(query=to_dev(wl.query, "bf16", dev), key=to_dev(wl.key, "bf16", dev),
+             value=to_dev(wl.value, "bf16", dev), key_cache=kc8, value_cache=vc8,
+             block_tables=torch.from_numpy(wl.block_tables).to(dev), seq_lens=torch.from_numpy(wl.seq_lens).to(dev),
+             positions=torch.from_numpy(wl.positions).to(dev),
+             query_start_loc=torch.from_numpy(wl.query_start_loc).to(dev))
+    slots, out = run_fp8_step(wl, t, decode=False)
+    r_slots = oracle.slot_mapping(wl.block_tables, wl.positions, wl.query_start_loc, sp.block_size, wl.num_blocks)
+    assert np.array_equal(slots.cpu().numpy(), r_slots), "slot mapping differs"
+    kc, vc = oracle.reshape_and_cache(wl.key, wl.value, wl.key_cache, wl.value_cache, r_slots)
+    bs = sp.block_size
+    got, ref = [], []
+    for s in pre_pick + dec_pick:
+        nblk = -(-int(wl.seq_lens[s]) // bs)
+        ids = [int(b) for b in wl.block_tables[s, :nblk]]
+        # free slots of the last block hold the bf16 NaN pattern: zeroed
+        # before quantising (they are never attended)
+        kb = np.where(kc[ids] == W.BF16_NAN, 0, kc[ids]).astype(np.uint16)
+        vb = np.where(vc[ids] == W.BF16_NAN, 0, vc[ids]).astype(np.uint16)
+        pk, pv = oracle.quantize_kv(kb, "bf16", K_SCALE), oracle.quantize_kv(vb, "bf16", V_SCALE)
+        # the new tokens' codes in the GPU pool are the oracle's
+        for tok in range(int(wl.query_start_loc[s]), int(wl.query_start_loc[s + 1])):
+            slot = int(r_slots[tok])
+            blk, off = divmod(slot, bs)
+            j = ids.index(blk)
+            assert np.array_equal(kc8[blk, off].cpu().numpy(), pk[j, off]), "K codes of a new token differ"
+            assert np.array_equal(vc8[blk, off].cpu().numpy(), pv[j, off]), "V codes of a new token differ"
+        table = np.full((1, wl.block_tables.shape[1]), -1, np.int32)
+        table[0, :nblk] = np.arange(nblk)
+        r0, r1 = int(wl.query_start_loc[s]), int(wl.query_start_loc[s + 1])
+        ref.append(oracle.varlen_attention(wl.query[r0:r1], pk, pv, table, wl.seq_lens[s:s + 1],
+                                           np.array([0, r1 - r0]), wl.scale, "bf16", (K_SCALE, V_SCALE)))
+        got.append(out[r0:r1])
+    assert_attn_close(torch.cat(got), np.concatenate(ref), "bf16", "config 5 E4M3 (sampled rows)")
+
+
 def test_fp8_precision_loss_against_unquantised_attention(dev):
     """The stated cost of FP8 pools: against float64 attention over the
     unquantised bf16 cache the error stays small (printed for the record)."""
