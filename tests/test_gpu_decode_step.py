@@ -145,17 +145,19 @@ def test_step_degenerate_rows_bitwise(fp8, dev):
     assert torch.count_nonzero(out[2]) == 0
 
 
-def test_step_matches_oracle_full_size(dev):
-    """The bench workload (128 sequences, 64/8 heads, lognormal lengths): the
-    one-call step against the oracle's write and float64 attention."""
-    wl = W.generate(3)
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_step_matches_oracle_full_size(cfg, dev):
+    """The decode workloads as the benchmark runs them (the tiny fp32 pair,
+    32 MHA sequences, 128 GQA sequences with lognormal lengths): the one-call
+    step against the oracle's write and float64 attention."""
+    wl = W.generate(cfg)
     t = upload(wl, dev)
     out = ops.decode_step(t["query"], t["key"], t["value"], t["key_cache"], t["value_cache"], t["block_tables"],
                           t["seq_lens"], wl.scale, wl.max_seq_len)
     torch.cuda.synchronize()
     _, r_kc, r_vc, r_out = oracle_step(wl)
     assert same_bits(t["key_cache"], r_kc) and same_bits(t["value_cache"], r_vc), "cache contents differ"
-    assert_attn_close(out, r_out, "bf16", "decode_step config 3")
+    assert_attn_close(out, r_out, wl.spec.dtype, "decode_step config %d" % cfg)
 
 
 @pytest.mark.parametrize("name", ["f32-gqa4-bs32", "gqa16-d64", "gqa32-d128-bs32"])

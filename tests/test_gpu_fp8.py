@@ -106,7 +106,26 @@ def test_fused_fp8_write_matches_oracle_bitwise(cfg, dev):
 
 # ------------------------------------------------------------------ attention over E4M3 pools
 def test_config3_full_size_fp8(dev):
-    _check(W.generate(3), dev, "gqa128")
+    """The 128-sequence batch over E4M3 pools, through the write + attention
+    calls and through the one-call step the benchmark times (on a copy of
+    the same pools), both against one oracle run."""
+    wl = W.generate(3)
+    log("[fp8 gqa128] seed %d: B=%d T=%d NB=%d maxL=%d" % (wl.seed, wl.num_seqs, wl.num_tokens, wl.num_blocks,
+                                                          wl.max_seq_len))
+    t = upload_fp8(wl, dev)
+    kc0, vc0 = t["key_cache"].clone(), t["value_cache"].clone()
+    slots, out = run_fp8_step(wl, t)
+    r_slots, r_kc, r_vc, r_out = oracle_fp8_step(wl, t)
+    assert np.array_equal(slots.cpu().numpy(), r_slots)
+    assert np.array_equal(t["key_cache"].cpu().numpy(), r_kc), "K codes differ"
+    assert np.array_equal(t["value_cache"].cpu().numpy(), r_vc), "V codes differ"
+    assert_attn_close(out, r_out, "bf16", "gqa128")
+    out1 = ops.decode_step_fp8(t["query"], t["key"], t["value"], kc0, vc0, t["block_tables"], t["seq_lens"],
+                               wl.scale, wl.max_seq_len, K_SCALE, V_SCALE)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc0.cpu().numpy(), r_kc), "K codes differ (decode_step_fp8)"
+    assert np.array_equal(vc0.cpu().numpy(), r_vc), "V codes differ (decode_step_fp8)"
+    assert_attn_close(out1, r_out, "bf16", "gqa128 decode_step_fp8")
 
 
 SMALL = {
