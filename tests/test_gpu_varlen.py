@@ -185,6 +185,39 @@ def test_one_launch_is_deterministic_and_leaves_its_counters_zero(dev):
     assert_attn_close(outs[0], r_out, wl.spec.dtype, "deterministic")
 
 
+def test_shared_workspace_across_calls(dev):
+    """Three varlen calls on one workspace: a 16-KV-head step (the prefill
+    kernel's per-XCD queues, two heads each), a smaller 8-head step, the
+    first again.  Each call rebuilds its item plan and queue counters, so
+    the repeated call is bit-identical and both steps match the oracle."""
+    wa = W.generate(SMALL["gqa2-kv16"], seed=46)
+    wb = W.generate(SMALL["gqa8-long-chunk"], seed=47)
+    ta, tb = upload(wa, dev), upload(wb, dev)
+    run_step(wa, ta, decode=False)                     # writes each step's K/V
+    run_step(wb, tb, decode=False)
+
+    def need(wl, t):
+        return ops.varlen_workspace_size(wl.num_seqs, wl.num_tokens, wl.spec.num_q_heads, wl.spec.num_kv_heads,
+                                         wl.spec.head_dim, wl.max_query_len, wl.spec.block_size, t["query"].dtype)
+
+    ws = torch.zeros(max(need(wa, ta), need(wb, tb)), dtype=torch.uint8, device=dev)
+
+    def call(wl, t):
+        out = ops.paged_attention_varlen(t["query"], t["key_cache"], t["value_cache"], t["block_tables"],
+                                         t["seq_lens"], t["query_start_loc"], wl.scale, wl.max_query_len,
+                                         wl.max_seq_len, workspace=ws)
+        torch.cuda.synchronize()
+        return out
+
+    with launches(single=False):
+        a1 = call(wa, ta)
+        b1 = call(wb, tb)
+        a2 = call(wa, ta)
+    assert torch.equal(a1.view(torch.int32), a2.view(torch.int32)), "repeated call differs"
+    assert_attn_close(a1, oracle_step(wa, decode=False)[3], wa.spec.dtype, "shared workspace, 16 KV heads")
+    assert_attn_close(b1, oracle_step(wb, decode=False)[3], wb.spec.dtype, "shared workspace, 8 KV heads")
+
+
 def test_decode_rows_equal_decode_call_bitwise(dev):
     """With the decode rows in their own launches, they run the decode
     call's kernels on the same split: bit-identical rows."""
